@@ -26,14 +26,14 @@ def test_uniform_block_draw_matches_single_draw():
 
 def test_integer_values():
     a = inputs.integer(200, 64, 3)
-    assert set(np.unique(a).tolist()) == {-2.0, -1.0, 0.0, 1.0, 2.0}
+    assert set(np.unique(a.astype(np.float32)).tolist()) == {-2.0, -1.0, 0.0, 1.0, 2.0}
     assert np.array_equal(a, inputs.integer(200, 64, 3))
 
 
 def test_hash_int_values():
     h = inputs.hash_int(64, 64, 1)
-    assert set(np.unique(h).tolist()) <= set(range(-3, 4))
-    assert len(np.unique(h)) == 7
+    assert set(np.unique(h.astype(np.float32)).tolist()) <= set(range(-3, 4))
+    assert len(np.unique(h.astype(np.float32))) == 7
     assert np.array_equal(h, inputs.hash_int(64, 64, 1))
 
 
