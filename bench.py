@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of C = A * B^T (fp16 in, fp32 accumulate/out) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8192^3]
+                    [--no-cpu-baseline] [--no-shapes]
+
+A step is one call of gemm_f16_f32_abt through the C ABI on synthetic
+operands already resident in HBM (uniform [-1, 1] fp16, seeds 1 and 2). The
+timed region is K back-to-back calls bracketed by device synchronisation;
+`value` is 2*M*N*K*K / elapsed in TFLOP/s. Each call is also bracketed by HIP
+events on the launch stream: their mean is the kernel's average launch
+duration, from which `roofline.achieved` is computed against the fp16 MFMA
+peak (2.5 PFLOP/s dense).
+
+Per-shape lines (`shapes`) time the five workloads the way "SASS-Level Kernel
+Generation for Blackwell" measures (section "How we measured"): every call
+runs alone (synchronised after each), the time of a call is its GPU time, and
+the median over the last N calls is reported, over sweeps run in forward then
+reverse order.
+
+`cpu_baseline` times the CPU reference (oracle/) on a bounded sample of the
+same workload: whole rows of C, as many as fit in about 10 s on the host's
+cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("TFLOP/s and µs/call per M×N×K (fp16→fp32 A·Bᵀ); "
+          "% of MI355X MFMA peak")
+PEAK_TFLOPS = 2500.0         # MI355X dense fp16 MFMA (published)
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E (published)
+# The pages' own number for this workload (one B200): 553.1 - 554.3 us at 8192^3.
+PAGE_US = {"8192^3": (553.1 + 554.3) / 2, "1024^3": (4.64 + 4.67) / 2,
+           "2048x2048x16384": (73.92 + 74.11) / 2, "1024x1024x65536": (76.93 + 77.22) / 2}
+CALLS = {"256^3": 400, "1024^3": 400, "2048x2048x16384": 200, "1024x1024x65536": 200,
+         "8192^3": 40}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_fp16_gemm_03_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(M, N, K):
+    flops = 2.0 * M * N * K
+    nbytes = 2.0 * (M * K + N * K) + 4.0 * M * N
+    return flops, nbytes
+
+
+def make_device_operands(torch, shape, dev):
+    from dense_fp16_gemm_03_amd import inputs
+
+    A, B = inputs.workload_operands(shape, "uniform")
+    return A, B, torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+
+
+def time_throughput(torch, gemm, At, Bt, C, steps, warmup):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        gemm.gemm_abt(At, Bt, C, stream=stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        gemm.gemm_abt(At, Bt, C, stream=stream)
+        e.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernel_ms = [s.elapsed_time(e) for s, e in ev]
+    return t1 - t0, kernel_ms
+
+
+def time_calls_alone(torch, gemm, At, Bt, C, calls, warmup=20):
+    """Median GPU time of a call when every call runs alone."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        gemm.gemm_abt(At, Bt, C, stream=stream)
+    torch.cuda.synchronize()
+    out = []
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(calls):
+        s.record(stream)
+        gemm.gemm_abt(At, Bt, C, stream=stream)
+        e.record(stream)
+        e.synchronize()
+        out.append(s.elapsed_time(e) * 1e3)
+    out.sort()
+    return out[len(out) // 2]
+
+
+def cpu_baseline(A, B, M, N, K, budget_s=10.0):
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.default_threads()
+    rows = max(1, threads)
+    t0 = time.perf_counter()
+    oracle.gemm_abt(A[:rows], B, threads=threads)
+    t = time.perf_counter() - t0
+    est = t / rows
+    rows2 = int(min(M, max(rows, budget_s / max(est, 1e-9))))
+    t0 = time.perf_counter()
+    oracle.gemm_abt(A[:rows2], B, threads=threads)
+    t = time.perf_counter() - t0
+    flops = 2.0 * rows2 * N * K
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{rows2 - 1} of C ({rows2}x{N}x{K}), {t:.1f} s, "
+                      f"binary64 triple loop on {threads} threads"}
+
+
+def traffic_for(workload, kernel_avg_s):
+    """HBM bytes per launch from committed rocprofv3 counters, if they match this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(workload)
+    if not entry or entry.get("source_hash") != source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="8192^3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-shapes", action="store_true")
+    ap.add_argument("--sweeps", type=int, default=2, help="forward/reverse sweeps for shapes")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from dense_fp16_gemm_03_amd import gemm, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    gemm.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    name = args.workload
+    M, N, K = inputs.WORKLOADS[name]
+    flops, nbytes = algorithmic(M, N, K)
+    log(f"[bench] workload {name}: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
+    A, B, At, Bt = make_device_operands(torch, (M, N, K), dev)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+    elapsed, kernel_ms = time_throughput(torch, gemm, At, Bt, C, args.steps, args.warmup)
+    ms_per_step = elapsed / args.steps * 1e3
+    value = flops * args.steps / elapsed / 1e12
+    avg_kernel_s = sum(kernel_ms) / len(kernel_ms) / 1e3
+    achieved = flops / avg_kernel_s / 1e12
+    log(f"[bench] {args.steps} steps in {elapsed * 1e3:.2f} ms: {value:.1f} TFLOP/s; "
+        f"kernel avg {avg_kernel_s * 1e6:.2f} us ({achieved:.1f} TFLOP/s)")
+    traffic = traffic_for(name, avg_kernel_s)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
+                "kernel_avg_us": round(avg_kernel_s * 1e6, 3),
+                "algorithmic_bytes": nbytes, "algorithmic_flops": flops}
+
+    shapes = []
+    if not args.no_shapes:
+        names = list(inputs.WORKLOADS)
+        results = {n: [] for n in names}
+        for sweep in range(args.sweeps):
+            order = names if sweep % 2 == 0 else names[::-1]
+            for n in order:
+                m, nn, k = inputs.WORKLOADS[n]
+                if n == name:
+                    a, b = At, Bt
+                    c = C
+                else:
+                    _, _, a, b = make_device_operands(torch, (m, nn, k), dev)
+                    c = torch.empty((m, nn), dtype=torch.float32, device=dev)
+                us = time_calls_alone(torch, gemm, a, b, c, CALLS[n])
+                results[n].append(us)
+                log(f"[bench] sweep {sweep} {n}: median {us:.2f} us/call")
+                del a, b, c
+                torch.cuda.empty_cache()
+        for n in names:
+            m, nn, k = inputs.WORKLOADS[n]
+            f, by = algorithmic(m, nn, k)
+            lo, hi = min(results[n]), max(results[n])
+            mid = (lo + hi) / 2
+            t_roof = max(f / (PEAK_TFLOPS * 1e12), by / (HBM_PEAK_GBS * 1e9))
+            entry = {"workload": n, "M": m, "N": nn, "K": k, "us_per_call": [round(lo, 3),
+                     round(hi, 3)], "tflops": round(f / (mid * 1e-6) / 1e12, 2),
+                     "bound": "mfma" if f / by > PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+                     else "hbm",
+                     "roofline_frac": round(t_roof / (mid * 1e-6), 4),
+                     "mfma_peak_frac": round(f / (mid * 1e-6) / 1e12 / PEAK_TFLOPS, 4),
+                     "calls": CALLS[n], "plan": gemm.gemm_f16_f32_abt_describe(m, nn, k)}
+            if n in PAGE_US:
+                entry["pages_b200_us"] = PAGE_US[n]
+            shapes.append(entry)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU reference on a sample ...")
+        cpu = cpu_baseline(A, B, M, N, K)
+        log(f"[bench] cpu: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
+
+    vs = None
+    if name in PAGE_US:
+        vs = round(value / (flops / (PAGE_US[name] * 1e-6) / 1e12), 4)
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": vs, "dtype": "f16",
+        "data": "synthetic: uniform[-1,1] fp16, seeds 1 (A) and 2 (B), resident in HBM",
+        "config": {"workload": f"gemm_abt {M}x{N}x{K}", "M": M, "N": N, "K": K,
+                   "accumulate": "f32", "output": "f32",
+                   "plan": gemm.gemm_f16_f32_abt_describe(M, N, K),
+                   "source_hash": source_hash()},
+        "roofline": roofline, "cpu_baseline": cpu, "shapes": shapes,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

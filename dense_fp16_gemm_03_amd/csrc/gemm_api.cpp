@@ -1,0 +1,418 @@
+// C ABI of libgemm_f16.so: argument checks, the shape -> plan rule, the
+// split-K / stream-K workspace, and kernel launch. Declarations and the
+// contract of every entry point are in include/gemm_f16.h.
+#include "gemm_f16.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "gemm_kernels.h"
+
+namespace {
+
+using namespace g16;
+
+constexpr int32_t kDefaultCUs = 256;  // MI355X: 8 XCDs x 32 CUs
+
+struct Plan {
+  int32_t kid = -1;       // tiled kernel id, KID_GENERAL, or -1 (nothing to do)
+  Sched s{};
+  bool c_vec4 = false;
+  size_t workspace = 0;   // bytes of flags + counts (0 if the schedule needs none)
+};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool ranges_overlap(const void* a, size_t abytes, const void* b, size_t bbytes) {
+  if (abytes == 0 || bbytes == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+size_t span_bytes(int64_t rows, int64_t ld, int64_t cols, size_t elem) {
+  if (rows <= 0 || cols <= 0) return 0;
+  return (size_t)((rows - 1) * ld + cols) * elem;
+}
+
+gemm_status_t validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                       const void* B, int64_t ldb, const float* C, int64_t ldc) {
+  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_VALUE;
+  if (lda < K || ldb < K || ldc < N) return GEMM_ERR_INVALID_VALUE;
+  if (M == 0 || N == 0) return GEMM_OK;
+  if (C == nullptr) return GEMM_ERR_INVALID_VALUE;
+  if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_INVALID_VALUE;
+  const size_t cbytes = span_bytes(M, ldc, N, 4);
+  if (K > 0 && (ranges_overlap(C, cbytes, A, span_bytes(M, lda, K, 2)) ||
+                ranges_overlap(C, cbytes, B, span_bytes(N, ldb, K, 2))))
+    return GEMM_ERR_INVALID_VALUE;
+  if (M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x7FFFFFFF) return GEMM_ERR_NOT_SUPPORTED;
+  if (((uintptr_t)A & 1) || ((uintptr_t)B & 1) || ((uintptr_t)C & 3))
+    return GEMM_ERR_NOT_SUPPORTED;
+  return GEMM_OK;
+}
+
+// Optional plan override for experiments: GEMM_F16_PLAN="kid=0,mode=1,splits=16,grid=256,group=4"
+// (any subset of keys). Read on every plan; unknown keys are ignored.
+struct Override {
+  int32_t kid = -1, mode = -1, splits = -1, grid = -1, group = -1;
+};
+
+Override read_override() {
+  Override o;
+  const char* env = std::getenv("GEMM_F16_PLAN");
+  if (!env) return o;
+  char buf[256];
+  std::snprintf(buf, sizeof(buf), "%s", env);
+  for (char* tok = std::strtok(buf, ","); tok; tok = std::strtok(nullptr, ",")) {
+    char key[32];
+    int val = 0;
+    if (std::sscanf(tok, "%31[^=]=%d", key, &val) != 2) continue;
+    if (!std::strcmp(key, "kid")) o.kid = val;
+    else if (!std::strcmp(key, "mode")) o.mode = val;
+    else if (!std::strcmp(key, "splits")) o.splits = val;
+    else if (!std::strcmp(key, "grid")) o.grid = val;
+    else if (!std::strcmp(key, "group")) o.group = val;
+  }
+  return o;
+}
+
+bool tiled_eligible(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                    int64_t ldb, int32_t kid) {
+  const KernelInfo* ki = kernel_info(kid);
+  if (!ki || K <= 0) return false;
+  if (((uintptr_t)A & 15) || ((uintptr_t)B & 15)) return false;
+  if (lda % 8 || ldb % 8 || K % 8) return false;
+  // Buffer offsets (row * ld + k, in bytes) must stay below 2^31.
+  const int64_t limit = (int64_t)1 << 31;
+  if ((int64_t)(ki->bm - 1) * lda * 2 + (K + ki->bk) * 2 >= limit) return false;
+  if ((int64_t)(ki->bn - 1) * ldb * 2 + (K + ki->bk) * 2 >= limit) return false;
+  (void)M;
+  (void)N;
+  return true;
+}
+
+// Shape -> kernel and schedule. The pages' rule (section "Inside the kernels"
+// of "SASS-Level Kernel Generation for Blackwell") picks per shape a tile, a
+// ring depth and how K is divided; this is the same kind of rule for 256 CUs:
+//   * enough 256x256 tiles to fill the CUs: 256x256, data-parallel,
+//     persistent grid walking the tiles by stride;
+//   * few tiles but long K: 256x256 with K split so tiles x splits fills
+//     the CUs (each share keeps >= 8 k-iterations);
+//   * small problems: smaller tiles, split K a little if K allows.
+Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+               int64_t ldb, const float* C, int64_t ldc, int32_t cus) {
+  Plan plan;
+  if (M == 0 || N == 0) return plan;
+  plan.c_vec4 = ((uintptr_t)C % 16 == 0) && (ldc % 4 == 0);
+  const Override o = read_override();
+
+  int32_t kid = KID_256x256x64_S2_W4;
+  int32_t mode = MODE_DATA_PARALLEL;
+  int32_t splits = 1;
+  {
+    const int64_t t256 = cdiv(M, 256) * cdiv(N, 256);
+    const int64_t k64 = cdiv(K, 64);
+    if (t256 >= cus) {
+      kid = KID_256x256x64_S2_W4;
+    } else if (t256 * k64 >= (int64_t)cus * 32) {
+      kid = KID_256x256x64_S2_W4;
+      splits = (int32_t)(cus / t256);
+      if (splits > k64 / 8) splits = (int32_t)(k64 / 8);
+      mode = splits > 1 ? MODE_SPLIT : MODE_DATA_PARALLEL;
+    } else {
+      const int64_t t128 = cdiv(M, 128) * cdiv(N, 128);
+      if (t128 * 4 >= cus || cdiv(M, 64) * cdiv(N, 64) < cus / 2) {
+        kid = t128 >= 16 ? KID_128x128x64_S4_W4 : KID_64x64x64_S4_W4;
+      } else {
+        kid = KID_64x64x64_S4_W4;
+      }
+      const KernelInfo* ki = kernel_info(kid);
+      const int64_t tiles = cdiv(M, ki->bm) * cdiv(N, ki->bn);
+      const int64_t kits = cdiv(K, ki->bk);
+      int64_t sp = tiles >= cus ? 1 : cus / tiles;
+      if (sp > kits / 4) sp = kits / 4;
+      if (sp < 1) sp = 1;
+      splits = (int32_t)sp;
+      mode = splits > 1 ? MODE_SPLIT : MODE_DATA_PARALLEL;
+    }
+  }
+  if (o.kid >= 0 && kernel_info(o.kid)) kid = o.kid;
+  if (o.mode >= 0 && o.mode <= MODE_STREAM_K) mode = o.mode;
+  if (o.splits >= 1) splits = o.splits;
+
+  if (!tiled_eligible(M, N, K, A, lda, B, ldb, kid)) {
+    plan.kid = KID_GENERAL;
+    return plan;
+  }
+  const KernelInfo* ki = kernel_info(kid);
+  Sched& s = plan.s;
+  s.tiles_m = (int32_t)cdiv(M, ki->bm);
+  s.tiles_n = (int32_t)cdiv(N, ki->bn);
+  const int64_t tiles = (int64_t)s.tiles_m * s.tiles_n;
+  s.k_iters = (int32_t)cdiv(K, ki->bk);
+  if (tiles > 0x3FFFFFFF || (int64_t)tiles * s.k_iters > ((int64_t)1 << 40)) {
+    plan.kid = KID_GENERAL;
+    return plan;
+  }
+  s.tiles = (int32_t)tiles;
+  s.group_m = o.group > 0 ? o.group : 4;
+  if (s.group_m > s.tiles_m) s.group_m = s.tiles_m;
+  s.mode = mode;
+  if (mode == MODE_SPLIT) {
+    if (splits > s.k_iters) splits = s.k_iters;
+    if (splits <= 1) s.mode = MODE_DATA_PARALLEL;
+  }
+  s.splits = s.mode == MODE_SPLIT ? splits : 1;
+
+  // Workgroups resident at once: one per CU for the tiled kernels.
+  const int64_t resident = cus;
+  int64_t units;
+  if (s.mode == MODE_STREAM_K) {
+    units = std::min<int64_t>((int64_t)tiles * s.k_iters, resident);
+  } else {
+    units = (int64_t)tiles * s.splits;
+  }
+  int64_t grid = std::min<int64_t>(units, resident);
+  if (o.grid > 0) grid = std::min<int64_t>(o.grid, s.mode == MODE_DATA_PARALLEL ? units : resident);
+  if (s.mode == MODE_STREAM_K) grid = std::min<int64_t>(grid, (int64_t)tiles * s.k_iters);
+  s.grid = (int32_t)std::max<int64_t>(grid, 1);
+  plan.kid = kid;
+  if (s.mode != MODE_DATA_PARALLEL) {
+    plan.workspace = (size_t)cdiv((int64_t)tiles * 2 * sizeof(uint32_t), 256) * 256;
+  }
+  return plan;
+}
+
+const char* mode_name(int32_t m) {
+  switch (m) {
+    case MODE_DATA_PARALLEL: return "data_parallel";
+    case MODE_SPLIT: return "split";
+    case MODE_STREAM_K: return "stream_k";
+    default: return "?";
+  }
+}
+
+// Device CU counts, cached per device.
+std::mutex g_mu;
+std::map<int, int32_t> g_cus;
+
+int32_t device_cus(int dev) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto it = g_cus.find(dev);
+  if (it != g_cus.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = kDefaultCUs;
+  g_cus[dev] = n;
+  return n;
+}
+
+// Library-owned workspaces, one per (device, stream), zero-filled at
+// allocation; kernels leave them zero when they finish.
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+gemm_status_t library_workspace(int dev, hipStream_t stream, size_t need, void** out) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  Workspace& w = g_ws[{dev, stream}];
+  if (w.bytes >= need) {
+    *out = w.ptr;
+    return GEMM_OK;
+  }
+  if (w.ptr) {
+    // Earlier calls on this stream may still use the old buffer.
+    if (hipStreamSynchronize(stream) != hipSuccess) return GEMM_ERR_HIP;
+    (void)hipFree(w.ptr);
+    w.ptr = nullptr;
+    w.bytes = 0;
+  }
+  size_t bytes = need < 65536 ? 65536 : need;
+  void* p = nullptr;
+  if (hipMalloc(&p, bytes) != hipSuccess) return GEMM_ERR_ALLOC;
+  if (hipMemset(p, 0, bytes) != hipSuccess) {
+    (void)hipFree(p);
+    return GEMM_ERR_HIP;
+  }
+  w.ptr = p;
+  w.bytes = bytes;
+  *out = p;
+  return GEMM_OK;
+}
+
+gemm_status_t run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                  int64_t ldb, float* C, int64_t ldc, bool caller_ws, void* ws, size_t ws_bytes,
+                  void* stream_v) {
+  gemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc);
+  if (st != GEMM_OK) return st;
+  if (M == 0 || N == 0) return GEMM_OK;
+  hipStream_t stream = (hipStream_t)stream_v;
+  int dev = 0;
+  if (caller_ws) {
+    // Checks on the caller's workspace come before any HIP call.
+    const Plan probe = make_plan(M, N, K, A, lda, B, ldb, C, ldc, kDefaultCUs);
+    if (probe.workspace > 0 && (ws == nullptr || ws_bytes < probe.workspace ||
+                                ((uintptr_t)ws & 255)))
+      return GEMM_ERR_WORKSPACE;
+  }
+  if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
+  const Plan plan = make_plan(M, N, K, A, lda, B, ldb, C, ldc, device_cus(dev));
+  GemmParams p{};
+  p.A = (const uint16_t*)A;
+  p.B = (const uint16_t*)B;
+  p.C = C;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldc = ldc;
+  p.M = (int32_t)M;
+  p.N = (int32_t)N;
+  p.K = (int32_t)K;
+  p.c_vec4 = plan.c_vec4 ? 1 : 0;
+  p.s = plan.s;
+  if (plan.kid == KID_GENERAL) {
+    return launch_general(p, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+  }
+  if (plan.workspace > 0) {
+    void* w = nullptr;
+    if (caller_ws) {
+      if (ws == nullptr || ws_bytes < plan.workspace || ((uintptr_t)ws & 255))
+        return GEMM_ERR_WORKSPACE;
+      w = ws;
+    } else {
+      st = library_workspace(dev, stream, plan.workspace, &w);
+      if (st != GEMM_OK) return st;
+    }
+    p.flags = (uint32_t*)w;
+  }
+  return launch_tiled(plan.kid, p, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+gemm_status_t gemm_f16_f32_abt(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                               const void* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+  return run(M, N, K, A, lda, B, ldb, C, ldc, false, nullptr, 0, stream);
+}
+
+size_t gemm_f16_f32_abt_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K < 0) return 0;
+  // Aligned operands with K as the row stride: the plan the fast path takes.
+  const void* aligned = (const void*)(uintptr_t)256;
+  const int64_t ld = K % 8 ? K + (8 - K % 8) : K;
+  const Plan plan = make_plan(M, N, K, aligned, ld, aligned, ld, (const float*)aligned, N,
+                              kDefaultCUs);
+  // The plan for other alignments never needs more than this many tiles.
+  return plan.workspace;
+}
+
+gemm_status_t gemm_f16_f32_abt_ws(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                  const void* B, int64_t ldb, float* C, int64_t ldc,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return run(M, N, K, A, lda, B, ldb, C, ldc, true, workspace, workspace_bytes, stream);
+}
+
+const char* gemm_status_string(gemm_status_t s) {
+  switch (s) {
+    case GEMM_OK: return "GEMM_OK";
+    case GEMM_ERR_INVALID_VALUE: return "GEMM_ERR_INVALID_VALUE: invalid argument";
+    case GEMM_ERR_NOT_SUPPORTED: return "GEMM_ERR_NOT_SUPPORTED: shape or alignment not supported";
+    case GEMM_ERR_HIP: return "GEMM_ERR_HIP: a HIP runtime call failed";
+    case GEMM_ERR_ALLOC: return "GEMM_ERR_ALLOC: workspace allocation failed";
+    case GEMM_ERR_WORKSPACE: return "GEMM_ERR_WORKSPACE: workspace too small or misaligned";
+    default: return "unknown gemm_status_t";
+  }
+}
+
+gemm_status_t gemm_f16_f32_abt_describe(int64_t M, int64_t N, int64_t K, char* buf, size_t len) {
+  if (buf == nullptr || len == 0) return GEMM_ERR_INVALID_VALUE;
+  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_VALUE;
+  const void* aligned = (const void*)(uintptr_t)256;
+  const int64_t ld = K % 8 ? K + (8 - K % 8) : K;
+  const Plan plan = make_plan(M, N, K, aligned, ld, aligned, ld, (const float*)aligned, N,
+                              kDefaultCUs);
+  if (plan.kid < 0) {
+    std::snprintf(buf, len, "M=%lld N=%lld K=%lld: nothing to do", (long long)M, (long long)N,
+                  (long long)K);
+  } else if (plan.kid == KID_GENERAL) {
+    std::snprintf(buf, len, "M=%lld N=%lld K=%lld kernel=general_64x64", (long long)M,
+                  (long long)N, (long long)K);
+  } else {
+    const KernelInfo* ki = kernel_info(plan.kid);
+    const Sched& s = plan.s;
+    std::snprintf(buf, len,
+                  "M=%lld N=%lld K=%lld kernel=%s kid=%d mode=%s splits=%d tiles=%d (%dx%d) "
+                  "k_iters=%d grid=%d group_m=%d lds=%d workspace=%zu",
+                  (long long)M, (long long)N, (long long)K, ki->name, plan.kid,
+                  mode_name(s.mode), s.splits, s.tiles, s.tiles_m, s.tiles_n, s.k_iters, s.grid,
+                  s.group_m, ki->lds_bytes, plan.workspace);
+  }
+  return GEMM_OK;
+}
+
+void gemm_f16_release_workspaces(void) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return;
+  std::lock_guard<std::mutex> lock(g_mu);
+  for (auto it = g_ws.begin(); it != g_ws.end();) {
+    if (it->first.first == dev) {
+      (void)hipStreamSynchronize(it->first.second);
+      (void)hipFree(it->second.ptr);
+      it = g_ws.erase(it);
+    } else {
+      ++it;
+    }
+  }
+}
+
+int64_t gemm_f16_schedule_dump(int64_t M, int64_t N, int64_t K, int64_t grid, int64_t* out,
+                               int64_t cap, int64_t* k_iters, int64_t* tiles) {
+  if (M <= 0 || N <= 0 || K <= 0 || cap < 0 || (cap > 0 && out == nullptr)) return -1;
+  const void* aligned = (const void*)(uintptr_t)256;
+  const int64_t ld = K % 8 ? K + (8 - K % 8) : K;
+  Plan plan = make_plan(M, N, K, aligned, ld, aligned, ld, (const float*)aligned, N, kDefaultCUs);
+  if (plan.kid < 0 || plan.kid == KID_GENERAL) return -1;
+  Sched s = plan.s;
+  if (grid > 0) {
+    if (s.mode == MODE_STREAM_K && grid > (int64_t)s.tiles * s.k_iters) return -1;
+    s.grid = (int32_t)grid;
+  }
+  if (k_iters) *k_iters = s.k_iters;
+  if (tiles) *tiles = s.tiles;
+  int64_t rows = 0;
+  for (int32_t w = 0; w < s.grid; ++w) {
+    const int32_t v = virtual_wg(w, s.grid);
+    Segment seg;
+    for (int32_t n = 0; seg_at(s, v, n, &seg); ++n) {
+      if (rows < cap) {
+        int64_t* r = out + rows * 6;
+        r[0] = w;
+        r[1] = seg.tile;
+        r[2] = seg.k_begin;
+        r[3] = seg.k_end;
+        r[4] = seg.role;
+        r[5] = seg.contributors;
+      }
+      ++rows;
+    }
+  }
+  return rows;
+}
+
+int64_t gemm_f16_wait_timeouts(void) {
+  unsigned long long n = 0;
+  if (hipDeviceSynchronize() != hipSuccess) return -1;
+  if (read_wait_timeouts(&n, false) != hipSuccess) return -1;
+  return (int64_t)n;
+}
+
+}  // extern "C"

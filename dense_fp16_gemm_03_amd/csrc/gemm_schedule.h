@@ -1,0 +1,133 @@
+// Persistent tile schedule shared by the device kernels and the host-side
+// schedule model (gemm_f16_schedule_dump). Every function here is plain
+// integer arithmetic, callable from both sides, so the model the tests check
+// is the very code the kernels run.
+//
+// Three modes, after the per-shape program rule of "SASS-Level Kernel
+// Generation for Blackwell" (section "Inside the kernels"):
+//   DATA_PARALLEL  each output tile is one unit over all of K; a fixed grid
+//                  walks the units by stride ("a fixed grid ... walking the
+//                  tiles by stride").
+//   SPLIT          K of every tile is cut into `splits` even shares ("K split
+//                  ... ways over the grid, adding in the L2").
+//   STREAM_K       the tiles' k-iterations, laid end to end, are cut into one
+//                  contiguous range per workgroup ("stream-K ... the CTA
+//                  holding a tile's first k step stores it, and the tile's
+//                  other CTAs add to it").
+// In SPLIT and STREAM_K the share holding a tile's first k-iteration stores
+// the tile and raises its flag; the others wait for the flag and add.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define G16_HD __host__ __device__ __forceinline__
+#else
+#define G16_HD inline
+#endif
+
+namespace g16 {
+
+enum SchedMode : int32_t { MODE_DATA_PARALLEL = 0, MODE_SPLIT = 1, MODE_STREAM_K = 2 };
+enum SegRole : int32_t { ROLE_ONLY = 0, ROLE_STORER = 1, ROLE_ADDER = 2 };
+
+struct Sched {
+  int32_t tiles_m, tiles_n, tiles;  // output tiles (tiles = tiles_m * tiles_n)
+  int32_t k_iters;                  // k-iterations (of BK) per tile
+  int32_t mode;                     // SchedMode
+  int32_t splits;                   // MODE_SPLIT: k-shares per tile (<= k_iters)
+  int32_t grid;                     // workgroups launched
+  int32_t group_m;                  // tile order: bands of group_m tile rows
+};
+
+struct Segment {
+  int32_t tile;        // position in tile order (also the flag index)
+  int32_t tm, tn;      // tile coordinates
+  int32_t k_begin;     // first k-iteration (inclusive)
+  int32_t k_end;       // last k-iteration (exclusive)
+  int32_t role;        // SegRole
+  int32_t contributors;
+};
+
+template <class T>
+G16_HD T min_of(T a, T b) { return a < b ? a : b; }
+template <class T>
+G16_HD T max_of(T a, T b) { return a > b ? a : b; }
+
+// Workgroups are handed to the 8 XCDs round-robin (workgroup w runs on XCD
+// w mod 8). Renumber them so each XCD gets a contiguous block of virtual
+// indices: neighbouring units then share an XCD and its L2.
+G16_HD int32_t virtual_wg(int32_t w, int32_t grid) {
+  if (grid % 8 != 0) return w;
+  return (w % 8) * (grid / 8) + w / 8;
+}
+
+// Tile order: bands of group_m tile rows, column-major inside a band, so a
+// run of consecutive indices covers a compact block of C.
+G16_HD void tile_coords(const Sched& s, int32_t idx, int32_t* tm, int32_t* tn) {
+  const int32_t per_band = s.group_m * s.tiles_n;
+  const int32_t band = idx / per_band;
+  const int32_t first_m = band * s.group_m;
+  const int32_t rows = min_of(s.tiles_m - first_m, s.group_m);
+  const int32_t r = idx - band * per_band;
+  *tm = first_m + r % rows;
+  *tn = r / rows;
+}
+
+// STREAM_K: first k-iteration (over all tiles) of virtual workgroup v.
+G16_HD int64_t sk_start(const Sched& s, int64_t v) {
+  const int64_t total = (int64_t)s.tiles * s.k_iters;
+  return v * total / s.grid;
+}
+
+// STREAM_K: the workgroup whose (non-empty) range holds iteration i.
+G16_HD int64_t sk_owner(const Sched& s, int64_t i) {
+  const int64_t total = (int64_t)s.tiles * s.k_iters;
+  return ((i + 1) * s.grid - 1) / total;
+}
+
+// Number of units (DATA_PARALLEL, SPLIT) or segments a workgroup walks is
+// found by iterating seg_at(...) until it returns false.
+//
+// DATA_PARALLEL / SPLIT: the n-th unit of virtual workgroup v is v + n*grid.
+// STREAM_K: the n-th segment of v, counted from the END of v's range, so the
+// segment that starts a tile (and stores it) comes first and never waits.
+G16_HD bool seg_at(const Sched& s, int32_t v, int32_t n, Segment* out) {
+  if (s.mode == MODE_STREAM_K) {
+    const int64_t a = sk_start(s, v);
+    int64_t b = sk_start(s, (int64_t)v + 1);
+    for (int32_t i = 0; b > a; ++i) {
+      const int64_t t = (b - 1) / s.k_iters;
+      const int64_t tile_lo = t * s.k_iters;
+      const int64_t lo = max_of(a, tile_lo);
+      if (i == n) {
+        out->tile = (int32_t)t;
+        tile_coords(s, (int32_t)t, &out->tm, &out->tn);
+        out->k_begin = (int32_t)(lo - tile_lo);
+        out->k_end = (int32_t)(b - tile_lo);
+        const int64_t first = sk_owner(s, tile_lo);
+        const int64_t last = sk_owner(s, tile_lo + s.k_iters - 1);
+        out->contributors = (int32_t)(last - first + 1);
+        out->role = out->contributors == 1 ? ROLE_ONLY
+                    : (out->k_begin == 0 ? ROLE_STORER : ROLE_ADDER);
+        return true;
+      }
+      b = lo;
+    }
+    return false;
+  }
+  const int32_t splits = s.mode == MODE_SPLIT ? s.splits : 1;
+  const int64_t u = (int64_t)v + (int64_t)n * s.grid;
+  if (u >= (int64_t)s.tiles * splits) return false;
+  const int32_t share = (int32_t)(u / s.tiles);
+  const int32_t t = (int32_t)(u - (int64_t)share * s.tiles);
+  out->tile = t;
+  tile_coords(s, t, &out->tm, &out->tn);
+  out->k_begin = (int32_t)((int64_t)share * s.k_iters / splits);
+  out->k_end = (int32_t)((int64_t)(share + 1) * s.k_iters / splits);
+  out->contributors = splits;
+  out->role = splits == 1 ? ROLE_ONLY : (share == 0 ? ROLE_STORER : ROLE_ADDER);
+  return true;
+}
+
+}  // namespace g16

@@ -1,0 +1,166 @@
+"""ctypes binding of libgemm_f16.so (see include/gemm_f16.h for the contract).
+
+The functions named like the C entry points take raw integers (device
+addresses, sizes, a hipStream_t as an int) and only marshal arguments.
+``gemm_abt`` is a convenience wrapper for torch tensors: torch supplies device
+memory and the current stream, the library does all the arithmetic. There is
+no fallback: if the library is missing or fails to load, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libgemm_f16.so")
+
+GEMM_OK = 0
+STATUS_NAMES = {
+    0: "GEMM_OK", 1: "GEMM_ERR_INVALID_VALUE", 2: "GEMM_ERR_NOT_SUPPORTED",
+    3: "GEMM_ERR_HIP", 4: "GEMM_ERR_ALLOC", 5: "GEMM_ERR_WORKSPACE",
+}
+
+# Every symbol include/gemm_f16.h declares.
+EXPORTS = (
+    "gemm_f16_f32_abt", "gemm_f16_f32_abt_workspace_size", "gemm_f16_f32_abt_ws",
+    "gemm_status_string", "gemm_f16_f32_abt_describe", "gemm_f16_release_workspaces",
+    "gemm_f16_schedule_dump", "gemm_f16_wait_timeouts",
+)
+
+_lib = None
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def load(path: str = LIBRARY):
+    """Load and bind the library (raises if it is missing)."""
+    global _lib
+    if _lib is not None and path == LIBRARY:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run __graft_entry__.build() or "
+                           "python -m dense_fp16_gemm_03_amd.build")
+    lib = ctypes.CDLL(path)
+    i64, p, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    st = ctypes.c_int
+    lib.gemm_f16_f32_abt.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
+    lib.gemm_f16_f32_abt.restype = st
+    lib.gemm_f16_f32_abt_workspace_size.argtypes = [i64, i64, i64]
+    lib.gemm_f16_f32_abt_workspace_size.restype = sz
+    lib.gemm_f16_f32_abt_ws.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, sz, p]
+    lib.gemm_f16_f32_abt_ws.restype = st
+    lib.gemm_status_string.argtypes = [st]
+    lib.gemm_status_string.restype = ctypes.c_char_p
+    lib.gemm_f16_f32_abt_describe.argtypes = [i64, i64, i64, ctypes.c_char_p, sz]
+    lib.gemm_f16_f32_abt_describe.restype = st
+    lib.gemm_f16_release_workspaces.argtypes = []
+    lib.gemm_f16_release_workspaces.restype = None
+    lib.gemm_f16_schedule_dump.argtypes = [i64, i64, i64, i64, p, i64, p, p]
+    lib.gemm_f16_schedule_dump.restype = i64
+    lib.gemm_f16_wait_timeouts.argtypes = []
+    lib.gemm_f16_wait_timeouts.restype = i64
+    if path == LIBRARY:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != GEMM_OK:
+        msg = load().gemm_status_string(status).decode()
+        raise GemmError(status, msg)
+
+
+# --- entry points with the C names (raw integers in, status checked) -------
+
+def gemm_f16_f32_abt(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    """Raw call; returns the status code (does not raise)."""
+    return load().gemm_f16_f32_abt(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f16_f32_abt_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
+                        stream=0) -> int:
+    return load().gemm_f16_f32_abt_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace,
+                                      workspace_bytes, stream)
+
+
+def gemm_f16_f32_abt_workspace_size(M, N, K) -> int:
+    return load().gemm_f16_f32_abt_workspace_size(M, N, K)
+
+
+def gemm_status_string(status: int) -> str:
+    return load().gemm_status_string(status).decode()
+
+
+def gemm_f16_f32_abt_describe(M, N, K) -> str:
+    buf = ctypes.create_string_buffer(512)
+    _check(load().gemm_f16_f32_abt_describe(M, N, K, buf, len(buf)))
+    return buf.value.decode()
+
+
+def gemm_f16_release_workspaces() -> None:
+    load().gemm_f16_release_workspaces()
+
+
+def gemm_f16_schedule_dump(M, N, K, grid=0):
+    """(rows, k_iters, tiles): rows is a list of
+    (workgroup, tile, k_begin, k_end, role, contributors)."""
+    import numpy as np
+
+    lib = load()
+    ki, nt = ctypes.c_int64(0), ctypes.c_int64(0)
+    n = lib.gemm_f16_schedule_dump(M, N, K, grid, None, 0, ctypes.byref(ki), ctypes.byref(nt))
+    if n < 0:
+        raise GemmError(1, "schedule_dump rejected the arguments")
+    out = np.zeros((max(n, 1), 6), dtype=np.int64)
+    n2 = lib.gemm_f16_schedule_dump(M, N, K, grid, out.ctypes.data, n, None, None)
+    assert n2 == n
+    return out[:n], ki.value, nt.value
+
+
+def gemm_f16_wait_timeouts() -> int:
+    return load().gemm_f16_wait_timeouts()
+
+
+# --- torch convenience -----------------------------------------------------
+
+def gemm_abt(A, B, C=None, stream=None, workspace=None):
+    """C = A @ B^T for torch tensors: A (M, K) and B (N, K) float16, C (M, N)
+    float32, all on one GPU with unit stride along the last dimension.
+    Returns C. Enqueued on ``stream`` (default: torch's current stream)."""
+    import torch
+
+    if A.dtype != torch.float16 or B.dtype != torch.float16:
+        raise TypeError("A and B must be float16")
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[1]:
+        raise ValueError("A must be (M, K) and B (N, K)")
+    M, K = A.shape
+    N = B.shape[0]
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if C.dtype != torch.float32 or tuple(C.shape) != (M, N):
+        raise ValueError("C must be float32 (M, N)")
+    for t, name in ((A, "A"), (B, "B"), (C, "C")):
+        if not t.is_cuda or t.device != A.device:
+            raise ValueError(f"{name} must be on A's GPU")
+        if t.shape[1] > 1 and t.stride(1) != 1 and t.numel() > 0:
+            raise ValueError(f"{name} must have unit stride along its last dimension")
+    lda = A.stride(0) if M > 1 else max(K, 1)
+    ldb = B.stride(0) if N > 1 else max(K, 1)
+    ldc = C.stride(0) if M > 1 else max(N, 1)
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device)
+    s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(A.device):
+        if workspace is None:
+            st = gemm_f16_f32_abt(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(),
+                                  ldc, s)
+        else:
+            st = gemm_f16_f32_abt_ws(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                                     C.data_ptr(), ldc, workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), s)
+    _check(st)
+    return C

@@ -1,0 +1,105 @@
+/*
+ * gemm_f16.h — C ABI of libgemm_f16.so: C = A * B^T on an AMD Instinct MI355X
+ * (gfx950), binary16 inputs, binary32 accumulation and output.
+ *
+ * The operation is the one "SASS-Level Kernel Generation for Blackwell"
+ * measures (section "The numbers", Setup): fp16 inputs, fp32 accumulation and
+ * output, C = A B^T. Nothing here depends on PyTorch; pointers are plain
+ * device (or host, where stated) addresses and sizes are element counts.
+ *
+ * Layouts (all row-major, elements):
+ *   A : M x K binary16, element (i, k) at A[i*lda + k]      (K contiguous)
+ *   B : N x K binary16, element (j, k) at B[j*ldb + k]      (K contiguous)
+ *   C : M x N binary32, element (i, j) at C[i*ldc + j]
+ *   C[i][j] = sum over k < K of A[i][k] * B[j][k], accumulated in binary32.
+ * C is overwritten (no alpha/beta; its prior contents never matter). K = 0
+ * writes zeros; M = 0 or N = 0 is a no-op.
+ *
+ * Execution: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) of the current HIP device and the call returns without waiting.
+ * The caller owns A, B, C and any workspace and keeps them alive until the
+ * stream work finishes. The library never frees or retains caller pointers.
+ * Argument errors are reported before any HIP call; device faults surface at
+ * the caller's next synchronisation. The library never aborts or prints.
+ */
+#ifndef GEMM_F16_H
+#define GEMM_F16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GEMM_OK = 0,
+  GEMM_ERR_INVALID_VALUE = 1, /* negative size, ld too small, NULL with work, C overlaps A/B */
+  GEMM_ERR_NOT_SUPPORTED = 2, /* shape/alignment outside what any kernel here handles */
+  GEMM_ERR_HIP = 3,           /* a HIP runtime call failed (launch, allocation of events...) */
+  GEMM_ERR_ALLOC = 4,         /* library-owned workspace could not be allocated */
+  GEMM_ERR_WORKSPACE = 5      /* caller workspace too small or misaligned */
+} gemm_status_t;
+
+/* C = A * B^T (see the layout block above). A, B, C are device pointers.
+ * Requirements: M, N, K >= 0; lda >= K; ldb >= K; ldc >= N; A, B, C non-NULL
+ * when M*N > 0 (A, B may be NULL when K = 0); C must not overlap A or B.
+ * Any alignment of pointers and strides is accepted: 16-byte aligned A, B
+ * with lda, ldb, K multiples of 8 take the tiled MFMA kernels, anything else
+ * a slower general kernel. Split-K / stream-K plans use a workspace the
+ * library allocates once per (device, stream) on first use; calls sharing a
+ * stream are ordered by it, calls on different streams do not share one. */
+gemm_status_t gemm_f16_f32_abt(int64_t M, int64_t N, int64_t K,
+                               const void* A, int64_t lda,
+                               const void* B, int64_t ldb,
+                               float* C, int64_t ldc, void* stream);
+
+/* Bytes of workspace gemm_f16_f32_abt_ws needs for this shape (0 if none). */
+size_t gemm_f16_f32_abt_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* As gemm_f16_f32_abt, with a caller-owned device workspace of at least
+ * gemm_f16_f32_abt_workspace_size(M, N, K) bytes, 256-byte aligned, which
+ * must be zero-filled before its first use. The library leaves it zero-filled
+ * again when each call's kernels finish, so it can be reused on the same
+ * stream without clearing. Two calls in flight at once must not share it.
+ * workspace may be NULL when the size is 0. */
+gemm_status_t gemm_f16_f32_abt_ws(int64_t M, int64_t N, int64_t K,
+                                  const void* A, int64_t lda,
+                                  const void* B, int64_t ldb,
+                                  float* C, int64_t ldc,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* gemm_status_string(gemm_status_t s);
+
+/* Writes a one-line description of the plan chosen for (M, N, K) into the
+ * host buffer buf (NUL-terminated, truncated to len). Touches no device. */
+gemm_status_t gemm_f16_f32_abt_describe(int64_t M, int64_t N, int64_t K, char* buf, size_t len);
+
+/* Frees the library-owned workspaces of the current device after waiting for
+ * their streams. Call only when no gemm on those streams is in flight. */
+void gemm_f16_release_workspaces(void);
+
+/* Host-side schedule model (no device is touched): fills out[] with one row
+ * of 6 int64 per (workgroup, segment) of the persistent schedule for
+ * (M, N, K) with `grid` workgroups (grid <= 0: the plan's own grid):
+ *   { workgroup, tile, k_iter_begin, k_iter_end, role, contributors }
+ * role 0 = only contributor (plain store), 1 = first k-share (plain store,
+ * then raises the tile's flag), 2 = later k-share (waits, then adds).
+ * Returns the number of rows (writes at most `cap`), or -1 on bad arguments.
+ * *k_iters and *tiles (if non-NULL) receive the plan's k-iterations per tile
+ * and its output-tile count. Used by tests to check that every (tile, k-iter)
+ * is covered exactly once and every shared tile has exactly one storer. */
+int64_t gemm_f16_schedule_dump(int64_t M, int64_t N, int64_t K, int64_t grid,
+                               int64_t* out, int64_t cap, int64_t* k_iters, int64_t* tiles);
+
+/* Number of flag waits that gave up after the bounded spin, summed over the
+ * library-owned workspaces of the current device (synchronises them). A
+ * non-zero value means a result computed during that time may be wrong. */
+int64_t gemm_f16_wait_timeouts(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_F16_H */

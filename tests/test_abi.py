@@ -1,0 +1,189 @@
+"""The C ABI without a GPU: exports, argument checks, plans and the schedule model.
+
+No call here launches work: argument errors return before any HIP call, and
+describe / schedule_dump are host-only.
+"""
+import os
+import re
+
+import numpy as np
+import pytest
+
+from dense_fp16_gemm_03_amd import gemm, inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_f16.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gemm.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = header_functions()
+    assert len(names) >= 8
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in gemm_f16.h but not exported"
+    assert sorted(gemm.EXPORTS) == names
+
+
+def test_status_strings(lib):
+    for code, name in gemm.STATUS_NAMES.items():
+        assert gemm.gemm_status_string(code).startswith(name)
+    assert "unknown" in gemm.gemm_status_string(99)
+
+
+# Fake device addresses: validation never dereferences them.
+A_PTR, B_PTR, C_PTR = 0x10000000, 0x20000000, 0x30000000
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((-1, 4, 4, A_PTR, 4, B_PTR, 4, C_PTR, 4), 1),          # negative M
+    ((4, 4, -2, A_PTR, 4, B_PTR, 4, C_PTR, 4), 1),          # negative K
+    ((4, 4, 8, A_PTR, 7, B_PTR, 8, C_PTR, 4), 1),           # lda < K
+    ((4, 4, 8, A_PTR, 8, B_PTR, 7, C_PTR, 4), 1),           # ldb < K
+    ((4, 5, 8, A_PTR, 8, B_PTR, 8, C_PTR, 4), 1),           # ldc < N
+    ((4, 4, 8, A_PTR, 8, B_PTR, 8, 0, 4), 1),               # C NULL with work
+    ((4, 4, 8, 0, 8, B_PTR, 8, C_PTR, 4), 1),               # A NULL with K > 0
+    ((4, 4, 8, A_PTR, 8, B_PTR, 8, A_PTR + 16, 4), 1),      # C overlaps A
+    ((4, 4, 8, A_PTR, 8, B_PTR, 8, B_PTR, 4), 1),           # C overlaps B
+    ((4, 4, 8, A_PTR + 1, 8, B_PTR, 8, C_PTR, 4), 2),       # A not 2-byte aligned
+    ((4, 4, 8, A_PTR, 8, B_PTR, 8, C_PTR + 2, 4), 2),       # C not 4-byte aligned
+    ((1 << 31, 4, 8, A_PTR, 8, B_PTR, 8, 1 << 44, 4), 2),   # M too large
+    ((0, 4, 8, A_PTR, 8, B_PTR, 8, C_PTR, 4), 0),           # M = 0: nothing to do
+    ((4, 0, 8, 0, 8, 0, 8, 0, 0), 0),                       # N = 0: nothing to do
+])
+def test_argument_checks(lib, args, expect):
+    assert gemm.gemm_f16_f32_abt(*args, 0) == expect
+
+
+def test_caller_workspace_checked_first(lib):
+    M, N, K = inputs.WORKLOADS["1024x1024x65536"]
+    need = gemm.gemm_f16_f32_abt_workspace_size(M, N, K)
+    assert need > 0
+    # too small / misaligned / NULL workspace: rejected before any HIP call
+    assert gemm.gemm_f16_f32_abt_ws(M, N, K, A_PTR, K, B_PTR, K, C_PTR, N, 0, 0, 0) == 5
+    assert gemm.gemm_f16_f32_abt_ws(M, N, K, A_PTR, K, B_PTR, K, C_PTR, N, 0x40000000,
+                                    need - 1, 0) == 5
+    assert gemm.gemm_f16_f32_abt_ws(M, N, K, A_PTR, K, B_PTR, K, C_PTR, N, 0x40000010,
+                                    need, 0) == 5
+
+
+def test_workspace_sizes(lib):
+    assert gemm.gemm_f16_f32_abt_workspace_size(8192, 8192, 8192) == 0
+    assert gemm.gemm_f16_f32_abt_workspace_size(0, 8, 8) == 0
+    ws = gemm.gemm_f16_f32_abt_workspace_size(2048, 2048, 16384)
+    assert ws > 0 and ws % 256 == 0
+
+
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_describe_workloads(lib, name):
+    M, N, K = inputs.WORKLOADS[name]
+    text = gemm.gemm_f16_f32_abt_describe(M, N, K)
+    assert f"M={M} N={N} K={K}" in text and "kernel=" in text
+
+
+def test_describe_general_and_empty(lib):
+    assert "general" in gemm.gemm_f16_f32_abt_describe(100, 100, 13)  # K % 8 != 0
+    assert "nothing" in gemm.gemm_f16_f32_abt_describe(0, 100, 13)
+
+
+# --- schedule model ----------------------------------------------------------
+
+def check_schedule(rows, k_iters, tiles):
+    """Every (tile, k-iteration) covered exactly once; a tile split among
+    several segments has exactly one storer (role 1) holding k = 0, the rest
+    adders (role 2); a whole tile is role 0; contributors == segment count."""
+    errors = []
+    cover = np.zeros((tiles, k_iters), dtype=np.int64)
+    per_tile = {}
+    for w, t, kb, ke, role, contrib in rows:
+        if not (0 <= t < tiles and 0 <= kb < ke <= k_iters):
+            errors.append(f"bad segment {(w, t, kb, ke)}")
+            continue
+        cover[t, kb:ke] += 1
+        per_tile.setdefault(t, []).append((kb, ke, role, contrib))
+    if not np.all(cover == 1):
+        bad = np.argwhere(cover != 1)[:3]
+        errors.append(f"coverage != 1 at (tile, k) {bad.tolist()}")
+    for t, segs in per_tile.items():
+        n = len(segs)
+        if any(c != n for _, _, _, c in segs):
+            errors.append(f"tile {t}: contributors field != {n}")
+        roles = sorted(r for _, _, r, _ in segs)
+        if n == 1 and roles != [0]:
+            errors.append(f"tile {t}: single segment with role {roles}")
+        if n > 1:
+            if roles != [1] + [2] * (n - 1):
+                errors.append(f"tile {t}: roles {roles}")
+            storer = [s for s in segs if s[2] == 1]
+            if storer and storer[0][0] != 0:
+                errors.append(f"tile {t}: storer does not hold k = 0")
+    if len(per_tile) != tiles:
+        errors.append(f"{tiles - len(per_tile)} tiles never scheduled")
+    return errors
+
+
+SCHED_CASES = [
+    (8192, 8192, 8192, None),
+    (2048, 2048, 16384, None),
+    (1024, 1024, 65536, None),
+    (1024, 1024, 1024, None),
+    (256, 256, 256, None),
+    (2048, 2048, 16384, "mode=2"),          # stream-K, even
+    (1000, 1500, 4104, "mode=2"),           # stream-K, ranges cross tile ends
+    (1000, 1500, 4104, "mode=2,grid=200"),
+    (777, 333, 1000, "mode=2,kid=4,grid=77"),
+    (5000, 300, 2048, "mode=1,splits=3"),
+    (3000, 2900, 1024, None),
+]
+
+
+@pytest.mark.parametrize("M,N,K,plan", SCHED_CASES)
+def test_schedule_covers_once(lib, monkeypatch, M, N, K, plan):
+    if plan:
+        monkeypatch.setenv("GEMM_F16_PLAN", plan)
+    rows, k_iters, tiles = gemm.gemm_f16_schedule_dump(M, N, K)
+    assert check_schedule(rows.tolist(), k_iters, tiles) == []
+    if plan and "mode=2" in plan:
+        assert "stream_k" in gemm.gemm_f16_f32_abt_describe(M, N, K)
+
+
+@pytest.mark.parametrize("M,N,K,plan", SCHED_CASES[:3] + SCHED_CASES[6:7])
+def test_schedule_model_detects_dropped_unit(lib, monkeypatch, M, N, K, plan):
+    """Dropping any one segment, or duplicating one, must fail the model."""
+    if plan:
+        monkeypatch.setenv("GEMM_F16_PLAN", plan)
+    rows, k_iters, tiles = gemm.gemm_f16_schedule_dump(M, N, K)
+    rows = rows.tolist()
+    rng = np.random.default_rng(5)
+    for i in rng.choice(len(rows), size=min(5, len(rows)), replace=False):
+        assert check_schedule(rows[:i] + rows[i + 1:], k_iters, tiles) != []
+        assert check_schedule(rows + [rows[i]], k_iters, tiles) != []
+
+
+def test_stream_k_storer_segment_first(lib, monkeypatch):
+    """In stream-K a workgroup walks its range from the end, so a segment that
+    starts a tile (and stores it) never comes after a segment that waits."""
+    monkeypatch.setenv("GEMM_F16_PLAN", "mode=2,grid=200")
+    rows, _, _ = gemm.gemm_f16_schedule_dump(1000, 1500, 4104)
+    by_wg = {}
+    for w, t, kb, ke, role, c in rows.tolist():
+        by_wg.setdefault(w, []).append(role)
+    for w, roles in by_wg.items():
+        if 2 in roles:
+            assert roles.index(2) == len(roles) - 1, f"workgroup {w} waits before storing"
+
+
+def test_grid_fits_one_workgroup_per_cu(lib):
+    """Split / stream-K plans wait on flags: their grid must be co-resident."""
+    for M, N, K in inputs.WORKLOADS.values():
+        rows, _, _ = gemm.gemm_f16_schedule_dump(M, N, K)
+        assert rows[:, 0].max() < 256

@@ -1,0 +1,317 @@
+"""GPU results against the CPU reference and closed forms (needs an MI355X).
+
+Every call goes through the C ABI (libgemm_f16.so) via the ctypes binding;
+torch only allocates device memory and provides streams.
+
+Bars:
+  * integer-valued inputs (|C| < 2^24, all partial sums exact in fp32):
+    bit-exact against the reference;
+  * uniform [-1, 1] inputs: |C_gpu - C_ref| <= 1e-5 * sum_k |a_ik b_jk| per
+    element (exact equality where that sum is 0).
+Full-size workloads are checked at sampled elements (whole rows and columns
+plus random points) against the reference, and in full against closed forms
+(A = I gives B^T, all-ones and k-block weights give known sums).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from dense_fp16_gemm_03_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+from dense_fp16_gemm_03_amd import gemm  # noqa: E402
+
+DEV = torch.device("cuda:0")
+WORKLOADS = inputs.WORKLOADS
+_cache = {}
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def operands(shape, kind):
+    key = (shape, kind)
+    if key not in _cache:
+        if len(_cache) > 6:
+            _cache.clear()
+        _cache[key] = inputs.workload_operands(shape, kind)
+    return _cache[key]
+
+
+def to_dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def run(A, B, fill=np.nan, **kw):
+    """gemm on the GPU; C pre-filled with `fill` (NaN by default: C must be overwritten)."""
+    At = A if isinstance(A, torch.Tensor) else to_dev(A)
+    Bt = B if isinstance(B, torch.Tensor) else to_dev(B)
+    C = torch.full((At.shape[0], Bt.shape[0]), fill, dtype=torch.float32, device=DEV)
+    gemm.gemm_abt(At, Bt, C, **kw)
+    torch.cuda.synchronize()
+    return C.cpu().numpy()
+
+
+def sample_points(M, N, n_rand=3000, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = [0, M - 1, M // 2, 257 % M]
+    cols = [0, N - 1, N // 2, 129 % N]
+    r = [np.full(N, i) for i in rows] + [np.arange(M) for _ in cols]
+    c = [np.arange(N) for _ in rows] + [np.full(M, j) for j in cols]
+    r.append(rng.integers(0, M, n_rand))
+    c.append(rng.integers(0, N, n_rand))
+    return np.concatenate(r), np.concatenate(c)
+
+
+def assert_exact(got, ref, what):
+    bad = got.astype(np.float64) != ref
+    if bad.any():
+        idx = np.argwhere(bad)[:5] if got.ndim == 2 else np.flatnonzero(bad)[:5]
+        raise AssertionError(f"{what}: {bad.sum()} mismatches, first at {idx.tolist()}")
+
+
+def assert_tol(got, ref, S, what):
+    ok = oracle.within_tolerance(got, ref, S)
+    err = np.abs(got.astype(np.float64) - ref) / np.where(S > 0, S, 1)
+    log(f"  {what}: max |err|/S = {err.max():.3e}")
+    if not ok.all():
+        idx = np.argwhere(~ok)[:5] if got.ndim == 2 else np.flatnonzero(~ok)[:5]
+        raise AssertionError(f"{what}: {(~ok).sum()} elements outside 1e-5*S, first {idx.tolist()}")
+
+
+@pytest.fixture(autouse=True)
+def _name(request, monkeypatch):
+    monkeypatch.delenv("GEMM_F16_PLAN", raising=False)
+    log(f"[gpu test] {request.node.name}")
+    yield
+
+
+# --- operand lane maps and the epilogue: closed forms -----------------------
+
+@pytest.mark.parametrize("n", [64, 256, 1024])
+def test_identity_left_and_right(n):
+    X = inputs.uniform(n, n, 31)
+    I = inputs.identity(n)
+    assert_exact(run(I, X), X.astype(np.float64).T, "A = I -> B^T")
+    assert_exact(run(X, I), X.astype(np.float64), "B = I -> A")
+
+
+def test_perm_pattern():
+    n = 512
+    P = inputs.perm_pattern(n, n)
+    assert_exact(run(inputs.identity(n), P), P.astype(np.float64).T, "A = I, B = perm")
+
+
+@pytest.mark.parametrize("name", ["8192^3"])
+def test_identity_full_size(name):
+    M, N, K = WORKLOADS[name]
+    B = operands((M, N, K), "uniform")[1]
+    log(f"  plan: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
+    assert_exact(run(inputs.identity(M, K), B), B.astype(np.float64).T, "A = I at 8192^3")
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_kblock_weighted_ones(name):
+    """A = 1, B[j][k] = 1 + (k//64 mod 7): C = sum of the weights. A missing or
+    doubled k-range (a split or stream-K share) changes every element."""
+    M, N, K = WORKLOADS[name]
+    log(f"  plan: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
+    w = 1 + (np.arange(K) // 64) % 7
+    expect = float(w.sum())
+    got = run(inputs.ones(M, K), inputs.kblock_weights(N, K, 64))
+    assert np.all(got == expect), f"k-block sum: expected {expect}, got {np.unique(got)[:5]}"
+
+
+# --- the five workloads against the reference -------------------------------
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+@pytest.mark.parametrize("kind", ["integer", "uniform"])
+def test_workload_parity(name, kind):
+    M, N, K = WORKLOADS[name]
+    A, B = operands((M, N, K), kind)
+    log(f"  plan: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
+    got = run(A, B)
+    assert np.isfinite(got).all(), "non-finite output (C not fully written?)"
+    if M * N * K <= 1024 ** 3:
+        ref, S = oracle.gemm_abt(A, B)
+        g = got
+    else:
+        rows, cols = sample_points(M, N)
+        ref, S = oracle.gemm_abt_elems(A, B, rows, cols)
+        g = got[rows, cols]
+    if kind == "integer":
+        assert_exact(g, ref, f"{name} integer")
+    else:
+        assert_tol(g, ref, S, f"{name} uniform")
+
+
+def test_hash_int_inputs():
+    """Integers in [-3, 3] from a hash of the index: exact."""
+    M, N, K = 1024, 1024, 4096
+    A, B = inputs.workload_operands((M, N, K), "hash_int")
+    ref, _ = oracle.gemm_abt(A, B)
+    assert_exact(run(A, B), ref, "hash_int")
+
+
+# --- ragged shapes, strides, alignment, degenerate cases --------------------
+
+RAGGED = [
+    (1000, 1300, 776),    # several tiles, ragged M, N and K tail (776 % 64 = 8)
+    (333, 517, 1096),
+    (1, 1, 8),
+    (1, 700, 64),
+    (700, 1, 64),
+    (65, 129, 8),
+    (257, 255, 4104),
+]
+
+
+@pytest.mark.parametrize("M,N,K", RAGGED)
+def test_ragged_shapes(M, N, K):
+    A = inputs.uniform(M, K, 101)
+    B = inputs.uniform(N, K, 102)
+    ref, S = oracle.gemm_abt(A, B)
+    log(f"  plan: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
+    assert_tol(run(A, B), ref, S, f"{M}x{N}x{K}")
+    Ai = inputs.integer(M, K, 103)
+    Bi = inputs.integer(N, K, 104)
+    ref, _ = oracle.gemm_abt(Ai, Bi)
+    assert_exact(run(Ai, Bi), ref, f"{M}x{N}x{K} integer")
+
+
+@pytest.mark.parametrize("M,N,K", [(100, 90, 13), (64, 64, 7), (300, 200, 1001), (5, 3, 1)])
+def test_general_kernel_odd_k(M, N, K):
+    assert "general" in gemm.gemm_f16_f32_abt_describe(M, N, K)
+    A = inputs.uniform(M, K, 111)
+    B = inputs.uniform(N, K, 112)
+    ref, S = oracle.gemm_abt(A, B)
+    assert_tol(run(A, B), ref, S, f"general {M}x{N}x{K}")
+
+
+def test_strided_and_unaligned_views():
+    M, N, K = 300, 200, 256
+    Abig = to_dev(inputs.integer(M, K + 24, 121))
+    Bbig = to_dev(inputs.integer(N, K + 40, 122))
+    for a0, b0 in ((0, 0), (8, 16), (1, 3)):  # (1, 3): not 16-byte aligned -> general kernel
+        a = Abig[:, a0:a0 + K]
+        b = Bbig[:, b0:b0 + K]
+        ref, _ = oracle.gemm_abt(a.cpu().numpy(), b.cpu().numpy())
+        assert_exact(run(a, b), ref, f"views offset {a0},{b0}")
+    # C with a row stride larger than N
+    Cbig = torch.full((M, N + 12), np.nan, dtype=torch.float32, device=DEV)
+    c = Cbig[:, 4:4 + N]
+    gemm.gemm_abt(Abig[:, :K], Bbig[:, :K], c)
+    torch.cuda.synchronize()
+    ref, _ = oracle.gemm_abt(Abig[:, :K].cpu().numpy(), Bbig[:, :K].cpu().numpy())
+    out = Cbig.cpu().numpy()
+    assert_exact(out[:, 4:4 + N], ref, "strided C")
+    assert np.isnan(out[:, :4]).all() and np.isnan(out[:, 4 + N:]).all(), "wrote outside C"
+
+
+def test_k_zero_writes_zeros():
+    A = torch.empty((37, 0), dtype=torch.float16, device=DEV)
+    B = torch.empty((41, 0), dtype=torch.float16, device=DEV)
+    got = run(A, B)
+    assert got.shape == (37, 41) and np.all(got == 0)
+
+
+def test_empty_m_or_n_is_noop():
+    for M, N in ((0, 5), (5, 0)):
+        C = torch.full((M, N), np.nan, dtype=torch.float32, device=DEV)
+        gemm.gemm_abt(torch.zeros((M, 16), dtype=torch.float16, device=DEV),
+                      torch.zeros((N, 16), dtype=torch.float16, device=DEV), C)
+    torch.cuda.synchronize()
+
+
+def test_subnormal_inputs():
+    """fp16 subnormals in A (B = 1): IEEE gives the exact sum; a flush to zero
+    would still be inside the tolerance. Records which one the MFMA does."""
+    M, N, K = 64, 64, 256
+    sub = np.arange(1, 1024, dtype=np.uint16)
+    A = np.resize(sub, M * K).reshape(M, K).view(np.float16)
+    B = inputs.ones(N, K)
+    ref, S = oracle.gemm_abt(A, B)
+    got = run(A, B)
+    exact = np.array_equal(got.astype(np.float64), ref)
+    log(f"  subnormal inputs: {'kept (IEEE)' if exact else 'NOT exact'}")
+    assert_tol(got, ref, S, "subnormals")
+
+
+# --- every kernel variant and schedule mode ---------------------------------
+
+PLANS = [f"kid={k}" for k in range(7)] + [
+    "kid=0,mode=1,splits=3", "kid=0,mode=2", "kid=0,mode=2,grid=37",
+    "kid=4,mode=2,grid=100", "kid=6,mode=1,splits=5", "kid=2,mode=2,grid=64",
+    "kid=1,mode=1,splits=2", "kid=3,mode=2,grid=29", "kid=5,mode=2,grid=130",
+]
+
+
+@pytest.mark.parametrize("plan", PLANS)
+def test_forced_plans(plan, monkeypatch):
+    monkeypatch.setenv("GEMM_F16_PLAN", plan)
+    M, N, K = 600, 520, 1352
+    log(f"  plan: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
+    Ai = inputs.integer(M, K, 131)
+    Bi = inputs.integer(N, K, 132)
+    ref, _ = oracle.gemm_abt(Ai, Bi)
+    assert_exact(run(Ai, Bi), ref, f"{plan} integer")
+    A = inputs.uniform(M, K, 133)
+    B = inputs.uniform(N, K, 134)
+    ref, S = oracle.gemm_abt(A, B)
+    assert_tol(run(A, B), ref, S, f"{plan} uniform")
+
+
+# --- invariants -------------------------------------------------------------
+
+def test_transpose_invariant():
+    M, N, K = 768, 512, 2048
+    Ai, Bi = inputs.integer(M, K, 141), inputs.integer(N, K, 142)
+    assert_exact(run(Bi, Ai), run(Ai, Bi).T.astype(np.float64), "integer transpose")
+    A, B = inputs.uniform(M, K, 143), inputs.uniform(N, K, 144)
+    ref, S = oracle.gemm_abt(A, B)
+    assert_tol(run(B, A).T, ref, S, "uniform transpose")
+
+
+@pytest.mark.parametrize("name", ["2048x2048x16384", "1024x1024x65536"])
+def test_repeat_and_workspace_returns_to_zero(name):
+    """Two calls give identical integer results (flags/counters left clean),
+    and a caller workspace is zero again after each call."""
+    M, N, K = WORKLOADS[name]
+    A, B = operands((M, N, K), "integer")
+    At, Bt = to_dev(A), to_dev(B)
+    first = run(At, Bt)
+    second = run(At, Bt, fill=-7.0)
+    assert np.array_equal(first, second)
+    nbytes = gemm.gemm_f16_f32_abt_workspace_size(M, N, K)
+    assert nbytes > 0
+    ws = torch.zeros(nbytes // 4, dtype=torch.int32, device=DEV)
+    for _ in range(2):
+        third = run(At, Bt, workspace=ws)
+        assert np.array_equal(first, third)
+        assert int(ws.count_nonzero().item()) == 0, "workspace not zero after the call"
+
+
+def test_non_default_stream():
+    M, N, K = WORKLOADS["1024x1024x65536"]
+    A, B = operands((M, N, K), "integer")
+    At, Bt = to_dev(A), to_dev(B)
+    ref = run(At, Bt)
+    s = torch.cuda.Stream()
+    C = torch.full((M, N), np.nan, dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        gemm.gemm_abt(At, Bt, C)
+    s.synchronize()
+    assert np.array_equal(C.cpu().numpy(), ref)
+
+
+def test_no_flag_wait_gave_up():
+    assert gemm.gemm_f16_wait_timeouts() == 0
