@@ -2,7 +2,7 @@
 """Benchmark of C = A * B^T (fp16 in, fp32 accumulate/out) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8192^3]
-                    [--no-cpu-baseline] [--no-shapes]
+                    [--no-cpu-baseline] [--shapes] [--calibrate-copy]
 
 A step is one call of gemm_f16_f32_abt through the C ABI on synthetic
 operands already resident in HBM (uniform [-1, 1] fp16, seeds 1 and 2). The
@@ -12,7 +12,7 @@ events on the launch stream: their mean is the kernel's average launch
 duration, from which `roofline.achieved` is computed against the fp16 MFMA
 peak (2.5 PFLOP/s dense).
 
-Per-shape lines (`shapes`) time the five workloads the way "SASS-Level Kernel
+With --shapes, per-shape lines (`shapes`) time the five workloads the way "SASS-Level Kernel
 Generation for Blackwell" measures (section "How we measured"): every call
 runs alone (synchronised after each), the time of a call is its GPU time, and
 the median over the last N calls is reported, over sweeps run in forward then
@@ -129,6 +129,19 @@ def cpu_baseline(A, B, M, N, K, budget_s=10.0):
                       f"binary64 triple loop on {threads} threads"}
 
 
+def calibrate_copy(torch):
+    """A plain copy of known size for scaling the HBM byte counters:
+    1 GiB fp32 read + 1 GiB written per launch (torch's elementwise kernel)."""
+    n = (1 << 30) // 4
+    x = torch.rand(n, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4,
+                      "launches": 5}), flush=True)
+
+
 def traffic_for(workload, kernel_avg_s):
     """HBM bytes per launch from committed rocprofv3 counters, if they match this source."""
     try:
@@ -149,7 +162,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="8192^3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-shapes", action="store_true")
+    ap.add_argument("--shapes", action="store_true",
+                    help="also time the five workloads, each call alone")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB fp32 copy kernel (counter calibration)")
     ap.add_argument("--sweeps", type=int, default=2, help="forward/reverse sweeps for shapes")
     args = ap.parse_args()
 
@@ -165,6 +181,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
     gemm.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -190,7 +209,7 @@ def main():
                 "algorithmic_bytes": nbytes, "algorithmic_flops": flops}
 
     shapes = []
-    if not args.no_shapes:
+    if args.shapes:
         names = list(inputs.WORKLOADS)
         results = {n: [] for n in names}
         for sweep in range(args.sweeps):
