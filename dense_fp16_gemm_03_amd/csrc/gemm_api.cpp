@@ -60,7 +60,7 @@ gemm_status_t validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t l
 // Optional plan override for experiments: GEMM_F16_PLAN="kid=0,mode=1,splits=16,grid=256,group=4"
 // (any subset of keys). Read on every plan; unknown keys are ignored.
 struct Override {
-  int32_t kid = -1, mode = -1, splits = -1, grid = -1, group = -1;
+  int32_t kid = -1, mode = -1, splits = -1, grid = -1, group = -1, xcd = -1;
 };
 
 Override read_override() {
@@ -78,6 +78,7 @@ Override read_override() {
     else if (!std::strcmp(key, "splits")) o.splits = val;
     else if (!std::strcmp(key, "grid")) o.grid = val;
     else if (!std::strcmp(key, "group")) o.group = val;
+    else if (!std::strcmp(key, "xcd")) o.xcd = val;
   }
   return o;
 }
@@ -163,6 +164,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
   s.tiles = (int32_t)tiles;
   s.group_m = o.group > 0 ? o.group : 4;
   if (s.group_m > s.tiles_m) s.group_m = s.tiles_m;
+  s.xcd_remap = o.xcd >= 0 ? (o.xcd != 0) : 1;
   s.mode = mode;
   if (mode == MODE_SPLIT) {
     if (splits > s.k_iters) splits = s.k_iters;
@@ -170,22 +172,25 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
   }
   s.splits = s.mode == MODE_SPLIT ? splits : 1;
 
-  // Workgroups resident at once: one per CU for the tiled kernels.
+  // Persistent grid: at most one workgroup per CU at a time (the tiled
+  // kernels' LDS use allows one per CU).
   const int64_t resident = cus;
-  int64_t units;
+  int64_t grid;
   if (s.mode == MODE_STREAM_K) {
-    units = std::min<int64_t>((int64_t)tiles * s.k_iters, resident);
+    grid = std::min<int64_t>((int64_t)tiles * s.k_iters, resident);
+    if (o.grid > 0) grid = std::min<int64_t>(grid, o.grid);
+  } else if (s.mode == MODE_SPLIT) {
+    grid = std::min<int64_t>((int64_t)tiles * s.splits, resident);
+    if (o.grid > 0) grid = std::min<int64_t>(grid, o.grid);
   } else {
-    units = (int64_t)tiles * s.splits;
+    grid = std::min<int64_t>(tiles, resident);
+    if (o.grid > 0) grid = std::min<int64_t>(o.grid, tiles);
   }
-  int64_t grid = std::min<int64_t>(units, resident);
-  if (o.grid > 0) grid = std::min<int64_t>(o.grid, s.mode == MODE_DATA_PARALLEL ? units : resident);
-  if (s.mode == MODE_STREAM_K) grid = std::min<int64_t>(grid, (int64_t)tiles * s.k_iters);
   s.grid = (int32_t)std::max<int64_t>(grid, 1);
+  s.slots = max_shares(s);
   plan.kid = kid;
-  if (s.mode != MODE_DATA_PARALLEL) {
-    plan.workspace = (size_t)cdiv((int64_t)tiles * 2 * sizeof(uint32_t), 256) * 256;
-  }
+  if (s.mode != MODE_DATA_PARALLEL)
+    plan.workspace = (size_t)((int64_t)tiles * s.slots * ki->bm * ki->bn * 4);
   return plan;
 }
 
@@ -213,8 +218,8 @@ int32_t device_cus(int dev) {
   return n;
 }
 
-// Library-owned workspaces, one per (device, stream), zero-filled at
-// allocation; kernels leave them zero when they finish.
+// Library-owned workspaces (partial tiles of split-K / stream-K plans), one
+// per (device, stream).
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -238,10 +243,6 @@ gemm_status_t library_workspace(int dev, hipStream_t stream, size_t need, void**
   size_t bytes = need < 65536 ? 65536 : need;
   void* p = nullptr;
   if (hipMalloc(&p, bytes) != hipSuccess) return GEMM_ERR_ALLOC;
-  if (hipMemset(p, 0, bytes) != hipSuccess) {
-    (void)hipFree(p);
-    return GEMM_ERR_HIP;
-  }
   w.ptr = p;
   w.bytes = bytes;
   *out = p;
@@ -290,7 +291,7 @@ gemm_status_t run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, c
       st = library_workspace(dev, stream, plan.workspace, &w);
       if (st != GEMM_OK) return st;
     }
-    p.flags = (uint32_t*)w;
+    p.partials = (f32x4_storage*)w;
   }
   return launch_tiled(plan.kid, p, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
@@ -351,10 +352,10 @@ gemm_status_t gemm_f16_f32_abt_describe(int64_t M, int64_t N, int64_t K, char* b
     const Sched& s = plan.s;
     std::snprintf(buf, len,
                   "M=%lld N=%lld K=%lld kernel=%s kid=%d mode=%s splits=%d tiles=%d (%dx%d) "
-                  "k_iters=%d grid=%d group_m=%d lds=%d workspace=%zu",
+                  "k_iters=%d grid=%d group_m=%d xcd_remap=%d slots=%d lds=%d workspace=%zu",
                   (long long)M, (long long)N, (long long)K, ki->name, plan.kid,
                   mode_name(s.mode), s.splits, s.tiles, s.tiles_m, s.tiles_n, s.k_iters, s.grid,
-                  s.group_m, ki->lds_bytes, plan.workspace);
+                  s.group_m, s.xcd_remap, s.slots, ki->lds_bytes, plan.workspace);
   }
   return GEMM_OK;
 }
@@ -390,17 +391,18 @@ int64_t gemm_f16_schedule_dump(int64_t M, int64_t N, int64_t K, int64_t grid, in
   if (tiles) *tiles = s.tiles;
   int64_t rows = 0;
   for (int32_t w = 0; w < s.grid; ++w) {
-    const int32_t v = virtual_wg(w, s.grid);
+    const int32_t v = virtual_wg(w, s.grid, s.xcd_remap);
     Segment seg;
     for (int32_t n = 0; seg_at(s, v, n, &seg); ++n) {
       if (rows < cap) {
-        int64_t* r = out + rows * 6;
+        int64_t* r = out + rows * 7;
         r[0] = w;
         r[1] = seg.tile;
         r[2] = seg.k_begin;
         r[3] = seg.k_end;
         r[4] = seg.role;
         r[5] = seg.contributors;
+        r[6] = seg.index;
       }
       ++rows;
     }
@@ -408,11 +410,5 @@ int64_t gemm_f16_schedule_dump(int64_t M, int64_t N, int64_t K, int64_t grid, in
   return rows;
 }
 
-int64_t gemm_f16_wait_timeouts(void) {
-  unsigned long long n = 0;
-  if (hipDeviceSynchronize() != hipSuccess) return -1;
-  if (read_wait_timeouts(&n, false) != hipSuccess) return -1;
-  return (int64_t)n;
-}
 
 }  // extern "C"

@@ -38,10 +38,8 @@ namespace g16 {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
-
-// Flag waits that gave up (see kSpinLimit); read by read_wait_timeouts().
-__device__ unsigned long long g_wait_timeouts = 0;
 
 namespace {
 
@@ -50,8 +48,7 @@ namespace {
 constexpr uint32_t kMaskedOffset = 0x80000000u;
 constexpr int32_t kNumRecords = 0x7FFFFFF0;
 constexpr int32_t kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
-// Polls of a tile flag before a waiting workgroup gives up (~seconds).
-constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr int kReduceThreads = 256;
 
 template <int BM_, int BN_, int BK_, int STAGES_, int WGM_, int WGN_>
 struct Cfg {
@@ -107,23 +104,18 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
 }
 
-// Wait until at most `pending` whole stages of this wave's loads are in flight.
-template <class C>
-__device__ __forceinline__ void wait_vm_stages(int pending) {
-  if constexpr (C::STAGES == 2) {
-    wait_vm<0>();
-  } else if constexpr (C::STAGES == 3) {
-    if (pending >= 1) wait_vm<C::LOADS>(); else wait_vm<0>();
-  } else if constexpr (C::STAGES == 4) {
-    if (pending >= 2) wait_vm<2 * C::LOADS>();
-    else if (pending == 1) wait_vm<C::LOADS>();
-    else wait_vm<0>();
-  } else {
-    static_assert(C::STAGES <= 4, "add a case");
-  }
-}
-
 __device__ __forceinline__ void wait_lgkm_zero() { __builtin_amdgcn_s_waitcnt(kLgkmZero); }
+
+// Workgroup barrier for the LDS ring: s_barrier alone. __syncthreads() would
+// also wait for every outstanding global load (its fence drains vmcnt), which
+// empties the prefetch ring at each stage; the waits the ring needs are the
+// explicit vmcnt / lgkmcnt ones placed before each call. The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <class C>
 struct Frags {
@@ -154,81 +146,224 @@ __device__ __forceinline__ void read_frags(const char* stage, int ks, int wm, in
   }
 }
 
-template <class C>
-__device__ __forceinline__ void mfma_step(const Frags<C>& f, f32x16 (&acc)[C::FM][C::FN]) {
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
-}
-
 // Buffer offsets (bytes, relative to the tile's first row at k = 0) of this
-// lane's 16-byte pieces of one stage, and the logical chunk each one holds.
+// lane's 16-byte pieces of one stage, and for each piece the bound its stage's
+// first k must stay below for the piece to be loaded (else it is masked and the
+// LDS slot is zero-filled without a memory access).
 template <class C, int LOADS_OF>
 struct LoadMap {
   uint32_t off[LOADS_OF];
-  int32_t chunk8[LOADS_OF];  // first k (relative to the stage) of the piece
+  int32_t lim[LOADS_OF];
 };
 
+// k_limit: loads cover k < k_limit only (the unit's k range, and K).
 template <class C, int LOADS_OF>
 __device__ __forceinline__ void make_load_map(LoadMap<C, LOADS_OF>& m, int wave, int lane,
-                                              int rows_valid, int64_t ld) {
+                                              int rows_valid, int64_t ld, int k_limit) {
 #pragma unroll
   for (int j = 0; j < LOADS_OF; ++j) {
     const int group = wave * LOADS_OF + j;
     const int row = group * C::RPL + lane / C::CHUNKS;
     const int chunk = swz<C::CHUNKS>(row, lane % C::CHUNKS);  // XOR: its own inverse
-    m.chunk8[j] = chunk * 8;
     m.off[j] = row < rows_valid ? (uint32_t)(row * ld * 2 + chunk * 16) : kMaskedOffset;
+    m.lim[j] = k_limit - chunk * 8;
   }
 }
 
-// Issue this wave's share of one stage: A pieces then B pieces.
-// k0 = first k of the stage; `tail` masks pieces at k >= K.
+struct Operands {
+  __amdgpu_buffer_rsrc_t ra, rb;
+};
+
+// Load j (A pieces first, then B pieces) of the stage whose first k is k0,
+// into the stage buffer `dst`.
 template <class C>
-__device__ __forceinline__ void issue_stage(char* stage, __amdgpu_buffer_rsrc_t ra,
-                                            __amdgpu_buffer_rsrc_t rb,
-                                            const LoadMap<C, C::A_LOADS>& ma,
-                                            const LoadMap<C, C::B_LOADS>& mb, int wave, int k0,
-                                            bool tail, int K) {
-  const int soff = k0 * 2;
-#pragma unroll
-  for (int j = 0; j < C::A_LOADS; ++j) {
-    uint32_t off = ma.off[j];
-    if (tail && k0 + ma.chunk8[j] >= K) off = kMaskedOffset;
+__device__ __forceinline__ void issue_one(int j, char* dst, const Operands& op,
+                                          const LoadMap<C, C::A_LOADS>& ma,
+                                          const LoadMap<C, C::B_LOADS>& mb, int wave, int k0) {
+  if (j < C::A_LOADS) {
+    const uint32_t off = k0 < ma.lim[j] ? ma.off[j] : kMaskedOffset;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        ra, (lds_void_ptr)(stage + (wave * C::A_LOADS + j) * 1024), 16, off, soff, 0, 0);
-  }
-#pragma unroll
-  for (int j = 0; j < C::B_LOADS; ++j) {
-    uint32_t off = mb.off[j];
-    if (tail && k0 + mb.chunk8[j] >= K) off = kMaskedOffset;
+        op.ra, (lds_void_ptr)(dst + (wave * C::A_LOADS + j) * 1024), 16, off, k0 * 2, 0, 0);
+  } else {
+    const int jb = j - C::A_LOADS;
+    const uint32_t off = k0 < mb.lim[jb] ? mb.off[jb] : kMaskedOffset;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rb, (lds_void_ptr)(stage + C::A_BYTES + (wave * C::B_LOADS + j) * 1024), 16, off, soff,
-        0, 0);
+        op.rb, (lds_void_ptr)(dst + C::A_BYTES + (wave * C::B_LOADS + jb) * 1024), 16, off,
+        k0 * 2, 0, 0);
   }
 }
 
-// Bounded wait for a tile's flag; counts a give-up in g_wait_timeouts.
-__device__ void wait_flag(uint32_t* flag) {
-  uint32_t polls = 0;
-  while (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != 1u) {
-    __builtin_amdgcn_s_sleep(2);
-    if (++polls == kSpinLimit) {
-      atomicAdd(&g_wait_timeouts, 1ull);
-      break;
+// How many of n items spread evenly over nm MFMAs fall after MFMA m.
+constexpr int items_at(int n, int nm, int m) {
+  int c = 0;
+  for (int r = 0; r < n; ++r) c += (r * nm / n == m);
+  return c;
+}
+
+// Scheduling groups for one k-step: MFMA m, then its reads, then its loads.
+template <int NM, int NR, int NL, int M>
+__device__ __forceinline__ void sched_pattern() {
+  if constexpr (M < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    constexpr int nr = items_at(NR, NM, M);
+    constexpr int nl = items_at(NL, NM, M);
+    if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);  // LDS reads
+    if constexpr (nl > 0) __builtin_amdgcn_sched_group_barrier(0x010, nl, 0);  // loads
+    sched_pattern<NM, NR, NL, M + 1>();
+  }
+}
+
+// One MFMA k-step on `cur`, interleaved with (a) the fragment reads of the
+// next k-step (k-step rks of stage buffer rstage) into `nxt` and (b) loads
+// [LFIRST, LFIRST + NL) of the stage being prefetched into lstage. The
+// scheduling groups pin the interleave: after each MFMA come the reads and
+// loads assigned to it, so neither the LDS reads nor the load issue (which
+// can stall while the address FIFO is full) holds back a run of MFMAs.
+template <class C, int LFIRST, int NL>
+__device__ __forceinline__ void kstep(f32x16 (&acc)[C::FM][C::FN], const Frags<C>& cur,
+                                      Frags<C>& nxt, const char* rstage, int rks, int wm, int wn,
+                                      int lane, char* lstage, const Operands& op,
+                                      const LoadMap<C, C::A_LOADS>& ma,
+                                      const LoadMap<C, C::B_LOADS>& mb, int wave, int k0) {
+  constexpr int NM = C::FM * C::FN;
+  constexpr int NR = C::FM + C::FN;
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const int i = m / C::FN, j = m % C::FN;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      if (r * NM / NR == m) {
+        if (r < C::FM) {
+          const int row = wm * C::WM + r * 32 + (lane & 31);
+          nxt.a[r] = *reinterpret_cast<const half8*>(rstage + frag_off<C>(row, rks, lane));
+        } else {
+          const int row = wn * C::WN + (r - C::FM) * 32 + (lane & 31);
+          nxt.b[r - C::FM] =
+              *reinterpret_cast<const half8*>(rstage + C::A_BYTES + frag_off<C>(row, rks, lane));
+        }
+      }
+    }
+#pragma unroll
+    for (int l = 0; l < NL; ++l)
+      if (NL > 0 && l * NM / NL == m) issue_one<C>(LFIRST + l, lstage, op, ma, mb, wave, k0);
+  }
+  sched_pattern<NM, NR, NL, 0>();
+}
+
+// The k-steps of one stage. K-steps 0..LK-1 also issue the loads of the stage
+// entering the ring (all in k-step 0 with a 2-deep ring, whose next stage must
+// land within this one). Before the last k-step the next stage is handed over
+// (its loads landed in every wave, all reads of the freed buffer done), and
+// that k-step reads the next stage's first fragments.
+template <class C, int KS>
+__device__ __forceinline__ void run_ksteps(f32x16 (&acc)[C::FM][C::FN], Frags<C> (&fr)[2],
+                                           const char* stage, const char* nstage, int wm, int wn,
+                                           int lane, char* lstage, const Operands& op,
+                                           const LoadMap<C, C::A_LOADS>& ma,
+                                           const LoadMap<C, C::B_LOADS>& mb, int wave, int k0) {
+  static_assert(C::KSTEPS % 2 == 0, "fragment double buffer alternates per k-step");
+  constexpr int LK = C::STAGES == 2 ? 1 : C::KSTEPS - 1;
+  constexpr int LF = KS < LK ? KS * C::LOADS / LK : 0;
+  constexpr int NL = KS < LK ? (KS + 1) * C::LOADS / LK - LF : 0;
+  if constexpr (KS < C::KSTEPS - 1) {
+    kstep<C, LF, NL>(acc, fr[KS & 1], fr[(KS + 1) & 1], stage, KS + 1, wm, wn, lane, lstage, op,
+                     ma, mb, wave, k0);
+    run_ksteps<C, KS + 1>(acc, fr, stage, nstage, wm, wn, lane, lstage, op, ma, mb, wave, k0);
+  } else {
+    wait_vm<C::LOADS * (C::STAGES - 2)>();
+    wait_lgkm_zero();
+    lds_barrier();
+    kstep<C, LF, NL>(acc, fr[KS & 1], fr[(KS + 1) & 1], nstage, 0, wm, wn, lane, lstage, op, ma,
+                     mb, wave, k0);
+  }
+}
+
+// Partial tiles in the workspace are kept in the accumulators' own layout:
+// float4 number (((i * FN + j) * 4 + g) * WAVES + wave) * 64 + lane holds
+// registers 4g..4g+3 of block (i, j) of that wave and lane, so each store and
+// each load of a wave covers 1 KiB of consecutive bytes.
+template <class C>
+__device__ __forceinline__ void write_partial(f32x4* part, const f32x16 (&acc)[C::FM][C::FN],
+                                              int wave, int lane) {
+  // Buffer stores: the tile's base in the descriptor, one per-lane offset, and
+  // each store's fixed offset in a scalar register (no per-store addresses).
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)part, (short)0, kNumRecords, kBufferWord3);
+  const int voff = (wave * 64 + lane) * 16;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                         acc[i][j][4 * g + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4, v), r, voff, ((i * C::FN + j) * 4 + g) * C::WAVES * 64 * 16,
+            0);
+      }
+}
+
+// Sums float4s [begin, end) of a tile's `shares` partials, over the shares in
+// k order, and writes them to C (the tile's rows m0.., columns n0..).
+template <class C>
+__device__ __forceinline__ void reduce_range(const GemmParams& p, const f32x4* parts, int shares,
+                                             int begin, int end, int m0, int n0) {
+  constexpr int L = C::BM * C::BN / 4;  // float4s per partial tile
+  constexpr int EB = 4;                 // elements per thread in flight
+  constexpr int CB = 4;                 // partials per element in flight
+  constexpr int T = kReduceThreads;
+  for (int e0 = begin + (int)threadIdx.x; e0 < end; e0 += T * EB) {
+    f32x4 sum[EB];
+#pragma unroll
+    for (int b = 0; b < EB; ++b) sum[b] = f32x4{};
+    for (int c0 = 0; c0 < shares; c0 += CB) {
+      f32x4 v[CB][EB];
+#pragma unroll
+      for (int cc = 0; cc < CB; ++cc)
+#pragma unroll
+        for (int b = 0; b < EB; ++b) {
+          const int e = e0 + b * T;
+          v[cc][b] = (c0 + cc < shares && e < end) ? parts[(int64_t)(c0 + cc) * L + e] : f32x4{};
+        }
+#pragma unroll
+      for (int cc = 0; cc < CB; ++cc)
+#pragma unroll
+        for (int b = 0; b < EB; ++b) sum[b] += v[cc][b];
+    }
+#pragma unroll
+    for (int b = 0; b < EB; ++b) {
+      const int e = e0 + b * T;
+      if (e >= end) continue;
+      const int lane = e % 64;
+      const int wave = (e / 64) % C::WAVES;
+      const int rest = e / (64 * C::WAVES);
+      const int g = rest % 4;
+      const int i = (rest / 4) / C::FN;
+      const int j = (rest / 4) % C::FN;
+      const int m = m0 + (wave / C::WGN) * C::WM + i * 32 + (lane & 31);
+      const int n = n0 + (wave % C::WGN) * C::WN + j * 32 + 8 * g + 4 * (lane >> 5);
+      if (m >= p.M) continue;
+      float* crow = p.C + (int64_t)m * p.ldc;
+      if (n + 3 < p.N && p.c_vec4) {
+        *reinterpret_cast<f32x4*>(crow + n) = sum[b];
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (n + q < p.N) crow[n + q] = sum[b][q];
+      }
     }
   }
 }
 
-// Write (role ONLY / STORER) or add (role ADDER) the wave's accumulators to C.
+// Write the wave's accumulators to C (a tile computed by one unit alone).
 // Lane l holds, for block (i, j) and register v = 4g + q:
 //   row    m = m_base + 32 i + l % 32
 //   column n = n_base + 32 j + 8 g + 4 (l / 32) + q
 template <class C>
 __device__ __forceinline__ void epilogue(const GemmParams& p, const f32x16 (&acc)[C::FM][C::FN],
-                                         int m_base, int n_base, int lane, bool add) {
+                                         int m_base, int n_base, int lane) {
   const bool full = m_base + C::WM <= p.M && n_base + C::WN <= p.N;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
@@ -241,18 +376,12 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const f32x16 (&acc
         const int n = n_base + j * 32 + 8 * g + 4 * (lane >> 5);
         const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                          acc[i][j][4 * g + 3]};
-        if (!add) {
-          if (full && p.c_vec4) {
-            *reinterpret_cast<f32x4*>(crow + n) = v;
-          } else if (m < p.M) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (n + q < p.N) crow[n + q] = v[q];
-          }
+        if (full && p.c_vec4) {
+          *reinterpret_cast<f32x4*>(crow + n) = v;
         } else if (m < p.M) {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            if (n + q < p.N) unsafeAtomicAdd(crow + n + q, v[q]);
+            if (n + q < p.N) crow[n + q] = v[q];
         }
       }
     }
@@ -270,26 +399,27 @@ void gemm_tiled_kernel(GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WGN;
   const int wn = wave % C::WGN;
-  const int v = virtual_wg(blockIdx.x, p.s.grid);
-  uint32_t* flags = p.flags;
-  uint32_t* counts = p.flags + p.s.tiles;
-  const bool k_tail = (p.K % C::BK) != 0;
+  const int v = virtual_wg(blockIdx.x, p.s.grid, p.s.xcd_remap);
 
   Segment seg;
   for (int n = 0; seg_at(p.s, v, n, &seg); ++n) {
     const int m0 = seg.tm * C::BM;
     const int n0 = seg.tn * C::BN;
     const int nk = seg.k_end - seg.k_begin;
+    // Loads cover this unit's k range only; the stages past its end that the
+    // ring still issues are fully masked (zero-filled, no memory access).
+    const int k_limit = min_of(p.K, seg.k_end * C::BK);
 
     // Operand windows for this tile: rows m0.. of A and n0.. of B.
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.A + (int64_t)m0 * p.lda), (short)0, kNumRecords, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.B + (int64_t)n0 * p.ldb), (short)0, kNumRecords, kBufferWord3);
+    Operands op;
+    op.ra = __builtin_amdgcn_make_buffer_rsrc((void*)(p.A + (int64_t)m0 * p.lda), (short)0,
+                                              kNumRecords, kBufferWord3);
+    op.rb = __builtin_amdgcn_make_buffer_rsrc((void*)(p.B + (int64_t)n0 * p.ldb), (short)0,
+                                              kNumRecords, kBufferWord3);
     LoadMap<C, C::A_LOADS> ma;
     LoadMap<C, C::B_LOADS> mb;
-    make_load_map<C, C::A_LOADS>(ma, wave, lane, p.M - m0, p.lda);
-    make_load_map<C, C::B_LOADS>(mb, wave, lane, p.N - n0, p.ldb);
+    make_load_map<C, C::A_LOADS>(ma, wave, lane, p.M - m0, p.lda, k_limit);
+    make_load_map<C, C::B_LOADS>(mb, wave, lane, p.N - n0, p.ldb, k_limit);
 
     f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -297,78 +427,71 @@ void gemm_tiled_kernel(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
 
-    // Every wave has finished reading LDS from the previous unit.
-    __syncthreads();
+    // The previous unit's loads have landed and every wave has finished
+    // reading LDS, so the ring buffers can be refilled.
+    wait_vm<0>();
+    wait_lgkm_zero();
+    lds_barrier();
 
-    const int last_kt = p.s.k_iters - 1;
 #pragma unroll
     for (int s = 0; s < C::STAGES - 1; ++s) {
-      if (s < nk) {
-        const int kt = seg.k_begin + s;
-        issue_stage<C>(smem + s * C::STAGE_BYTES, ra, rb, ma, mb, wave, kt * C::BK,
-                       k_tail && kt == last_kt, p.K);
-      }
-    }
-
-    Frags<C> cur, nxt;
-    if (nk > 0) {
-      wait_vm_stages<C>(min_of(C::STAGES - 2, nk - 1));
-      __syncthreads();
-      read_frags<C>(smem, 0, wm, wn, lane, cur);
-    }
-
-    for (int it = 0; it < nk; ++it) {
-      const int st = it % C::STAGES;
-      const char* stage = smem + st * C::STAGE_BYTES;
-      // The buffer of iteration it-1 was released at the last barrier.
-      if (it + C::STAGES - 1 < nk) {
-        const int kt = seg.k_begin + it + C::STAGES - 1;
-        issue_stage<C>(smem + ((it + C::STAGES - 1) % C::STAGES) * C::STAGE_BYTES, ra, rb, ma,
-                       mb, wave, kt * C::BK, k_tail && kt == last_kt, p.K);
-      }
 #pragma unroll
-      for (int ks = 0; ks < C::KSTEPS - 1; ++ks) {
-        read_frags<C>(stage, ks + 1, wm, wn, lane, nxt);
-        mfma_step<C>(cur, acc);
-        cur = nxt;
-      }
-      if (it + 1 < nk) {
-        // Hand over the next stage, then start its first reads while the
-        // last k-step of this stage runs on the matrix cores.
-        wait_vm_stages<C>(min_of(C::STAGES - 2, nk - 2 - it));
-        wait_lgkm_zero();
-        __syncthreads();
-        read_frags<C>(smem + ((it + 1) % C::STAGES) * C::STAGE_BYTES, 0, wm, wn, lane, nxt);
-      }
-      mfma_step<C>(cur, acc);
-      cur = nxt;
+      for (int j = 0; j < C::LOADS; ++j)
+        issue_one<C>(j, smem + s * C::STAGE_BYTES, op, ma, mb, wave, (seg.k_begin + s) * C::BK);
     }
 
-    const int m_base = m0 + wm * C::WM;
-    const int n_base = n0 + wn * C::WN;
-    if (seg.role != ROLE_ADDER) {
-      epilogue<C>(p, acc, m_base, n_base, lane, false);
-      if (seg.role == ROLE_STORER) {
-        __syncthreads();
-        if (tid == 0) __hip_atomic_store(&flags[seg.tile], 1u, __ATOMIC_RELEASE,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-      }
+    Frags<C> fr[2];
+    wait_vm<C::LOADS * (C::STAGES - 2)>();
+    lds_barrier();
+    read_frags<C>(smem, 0, wm, wn, lane, fr[0]);
+
+    int st = 0;  // ring buffer holding stage `it`
+    for (int it = 0; it < nk; ++it) {
+      const int st_next = st + 1 == C::STAGES ? 0 : st + 1;
+      const int st_load = st == 0 ? C::STAGES - 1 : st - 1;  // freed at the last barrier
+      const char* stage = smem + st * C::STAGE_BYTES;
+      char* lstage = smem + st_load * C::STAGE_BYTES;
+      const int k0_load = (seg.k_begin + it + C::STAGES - 1) * C::BK;
+      run_ksteps<C, 0>(acc, fr, stage, smem + st_next * C::STAGE_BYTES, wm, wn, lane, lstage, op,
+                       ma, mb, wave, k0_load);
+      st = st_next;
+    }
+
+    if (seg.role == ROLE_ONLY) {
+      epilogue<C>(p, acc, m0 + wm * C::WM, n0 + wn * C::WN, lane);
     } else {
-      if (tid == 0) wait_flag(&flags[seg.tile]);
-      __syncthreads();
-      epilogue<C>(p, acc, m_base, n_base, lane, true);
-      __syncthreads();
-      if (tid == 0) {
-        const uint32_t before = __hip_atomic_fetch_add(&counts[seg.tile], 1u, __ATOMIC_ACQ_REL,
-                                                       __HIP_MEMORY_SCOPE_AGENT);
-        if (before == (uint32_t)(seg.contributors - 2)) {
-          // Last adder: every adder has seen the flag; leave both words zero.
-          __hip_atomic_store(&counts[seg.tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(&flags[seg.tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
+      // One share of a tile: its partial goes to the workspace; the reduce
+      // kernel that follows on the stream sums the shares into C.
+      write_partial<C>(p.partials + ((int64_t)seg.tile * p.s.slots + seg.index) * (C::BM * C::BN / 4),
+                       acc, wave, lane);
     }
   }
+}
+
+// Shares of output tile t under schedule s (1: the tile was stored directly).
+__device__ __forceinline__ int tile_shares(const Sched& s, int t) {
+  if (s.mode == MODE_SPLIT) return s.splits;
+  if (s.mode != MODE_STREAM_K) return 1;
+  const int64_t lo = (int64_t)t * s.k_iters;
+  return (int)(sk_owner(s, lo + s.k_iters - 1) - sk_owner(s, lo) + 1);
+}
+
+// Reduce pass for split-K / stream-K: workgroup b handles slice b % slices
+// of tile b / slices. Partials are summed in k order, so the result does not
+// depend on timing.
+template <class C>
+__global__ __launch_bounds__(kReduceThreads) void gemm_reduce_kernel(GemmParams p, int32_t slices) {
+  constexpr int L = C::BM * C::BN / 4;
+  const int t = blockIdx.x / slices;
+  const int slice = blockIdx.x % slices;
+  const int shares = tile_shares(p.s, t);
+  if (shares <= 1) return;
+  int tm, tn;
+  tile_coords(p.s, t, &tm, &tn);
+  const int begin = (int)((int64_t)slice * L / slices);
+  const int end = (int)((int64_t)(slice + 1) * L / slices);
+  reduce_range<C>(p, p.partials + (int64_t)t * p.s.slots * L, shares, begin, end, tm * C::BM,
+                  tn * C::BN);
 }
 
 // General kernel: any shape, stride and (element-natural) alignment. One
@@ -419,6 +542,9 @@ using C3 = Cfg<256, 128, 64, 3, 2, 2>;
 using C4 = Cfg<128, 128, 64, 4, 2, 2>;
 using C5 = Cfg<128, 64, 64, 4, 2, 2>;
 using C6 = Cfg<64, 64, 64, 4, 2, 2>;
+using C7 = Cfg<256, 256, 32, 5, 2, 2>;
+using C8 = Cfg<256, 256, 32, 4, 2, 4>;
+using C9 = Cfg<256, 256, 32, 5, 2, 4>;
 
 template <class C>
 constexpr KernelInfo info_of(const char* name) {
@@ -429,12 +555,22 @@ constexpr KernelInfo kInfos[KID_COUNT] = {
     info_of<C0>("256x256x64_s2_w4"), info_of<C1>("256x256x32_s4_w4"),
     info_of<C2>("256x256x64_s2_w8"), info_of<C3>("256x128x64_s3_w4"),
     info_of<C4>("128x128x64_s4_w4"), info_of<C5>("128x64x64_s4_w4"),
-    info_of<C6>("64x64x64_s4_w4"),
+    info_of<C6>("64x64x64_s4_w4"), info_of<C7>("256x256x32_s5_w4"),
+    info_of<C8>("256x256x32_s4_w8"), info_of<C9>("256x256x32_s5_w8"),
 };
 
 template <class C>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(gemm_tiled_kernel<C>, dim3(p.s.grid), dim3(C::THREADS), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.s.mode == MODE_DATA_PARALLEL) return e;
+  // Slices per tile: enough workgroups to cover the CUs, at least 4 KiB each.
+  const int max_slices = C::BM * C::BN / 4 / 256;
+  int slices = (256 + p.s.tiles - 1) / p.s.tiles;
+  if (slices > max_slices) slices = max_slices;
+  if (slices < 1) slices = 1;
+  hipLaunchKernelGGL(gemm_reduce_kernel<C>, dim3(p.s.tiles * slices), dim3(kReduceThreads), 0,
+                     stream, p, slices);
   return hipGetLastError();
 }
 
@@ -463,6 +599,9 @@ hipError_t launch_tiled(int32_t kid, const GemmParams& p, hipStream_t stream) {
     case KID_128x128x64_S4_W4: return launch_cfg<C4>(p, stream);
     case KID_128x64x64_S4_W4: return launch_cfg<C5>(p, stream);
     case KID_64x64x64_S4_W4: return launch_cfg<C6>(p, stream);
+    case KID_256x256x32_S5_W4: return launch_cfg<C7>(p, stream);
+    case KID_256x256x32_S4_W8: return launch_cfg<C8>(p, stream);
+    case KID_256x256x32_S5_W8: return launch_cfg<C9>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -476,6 +615,9 @@ int32_t tiled_occupancy(int32_t kid) {
     case KID_128x128x64_S4_W4: return occupancy_cfg<C4>();
     case KID_128x64x64_S4_W4: return occupancy_cfg<C5>();
     case KID_64x64x64_S4_W4: return occupancy_cfg<C6>();
+    case KID_256x256x32_S5_W4: return occupancy_cfg<C7>();
+    case KID_256x256x32_S4_W8: return occupancy_cfg<C8>();
+    case KID_256x256x32_S5_W8: return occupancy_cfg<C9>();
     default: return 0;
   }
 }
@@ -489,15 +631,6 @@ hipError_t launch_general(const GemmParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(gemm_general_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, p,
                      (int32_t)tiles_n);
   return hipGetLastError();
-}
-
-hipError_t read_wait_timeouts(unsigned long long* out, bool reset) {
-  hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_wait_timeouts), sizeof(*out), 0,
-                                     hipMemcpyDeviceToHost);
-  if (e != hipSuccess || !reset) return e;
-  const unsigned long long zero = 0;
-  return hipMemcpyToSymbol(HIP_SYMBOL(g_wait_timeouts), &zero, sizeof(zero), 0,
-                           hipMemcpyHostToDevice);
 }
 
 }  // namespace g16

@@ -14,8 +14,12 @@
 //                  contiguous range per workgroup ("stream-K ... the CTA
 //                  holding a tile's first k step stores it, and the tile's
 //                  other CTAs add to it").
-// In SPLIT and STREAM_K the share holding a tile's first k-iteration stores
-// the tile and raises its flag; the others wait for the flag and add.
+// A tile whose k-iterations are shared among several workgroups is reduced
+// through the workspace: every share writes its fp32 partial tile, and once
+// all shares of the tile have arrived each one sums a slice of the tile over
+// all partials, in k order, and writes that slice of C. Shared tiles occur
+// only in schedules where all of a tile's shares run at once (one unit per
+// workgroup in SPLIT; one range per workgroup in STREAM_K).
 #pragma once
 
 #include <stdint.h>
@@ -29,7 +33,7 @@
 namespace g16 {
 
 enum SchedMode : int32_t { MODE_DATA_PARALLEL = 0, MODE_SPLIT = 1, MODE_STREAM_K = 2 };
-enum SegRole : int32_t { ROLE_ONLY = 0, ROLE_STORER = 1, ROLE_ADDER = 2 };
+enum SegRole : int32_t { ROLE_ONLY = 0, ROLE_SHARED = 1 };
 
 struct Sched {
   int32_t tiles_m, tiles_n, tiles;  // output tiles (tiles = tiles_m * tiles_n)
@@ -38,6 +42,8 @@ struct Sched {
   int32_t splits;                   // MODE_SPLIT: k-shares per tile (<= k_iters)
   int32_t grid;                     // workgroups launched
   int32_t group_m;                  // tile order: bands of group_m tile rows
+  int32_t xcd_remap;                // 1: renumber workgroups XCD by XCD (virtual_wg)
+  int32_t slots;                    // partial-tile slots per tile in the workspace
 };
 
 struct Segment {
@@ -46,7 +52,8 @@ struct Segment {
   int32_t k_begin;     // first k-iteration (inclusive)
   int32_t k_end;       // last k-iteration (exclusive)
   int32_t role;        // SegRole
-  int32_t contributors;
+  int32_t contributors;  // shares of this tile (1 for ROLE_ONLY)
+  int32_t index;         // this share's position among them, in k order
 };
 
 template <class T>
@@ -57,8 +64,8 @@ G16_HD T max_of(T a, T b) { return a > b ? a : b; }
 // Workgroups are handed to the 8 XCDs round-robin (workgroup w runs on XCD
 // w mod 8). Renumber them so each XCD gets a contiguous block of virtual
 // indices: neighbouring units then share an XCD and its L2.
-G16_HD int32_t virtual_wg(int32_t w, int32_t grid) {
-  if (grid % 8 != 0) return w;
+G16_HD int32_t virtual_wg(int32_t w, int32_t grid, int32_t remap = 1) {
+  if (!remap || grid % 8 != 0) return w;
   return (w % 8) * (grid / 8) + w / 8;
 }
 
@@ -90,8 +97,7 @@ G16_HD int64_t sk_owner(const Sched& s, int64_t i) {
 // found by iterating seg_at(...) until it returns false.
 //
 // DATA_PARALLEL / SPLIT: the n-th unit of virtual workgroup v is v + n*grid.
-// STREAM_K: the n-th segment of v, counted from the END of v's range, so the
-// segment that starts a tile (and stores it) comes first and never waits.
+// STREAM_K: the n-th segment of v, counted from the end of v's range.
 G16_HD bool seg_at(const Sched& s, int32_t v, int32_t n, Segment* out) {
   if (s.mode == MODE_STREAM_K) {
     const int64_t a = sk_start(s, v);
@@ -108,8 +114,8 @@ G16_HD bool seg_at(const Sched& s, int32_t v, int32_t n, Segment* out) {
         const int64_t first = sk_owner(s, tile_lo);
         const int64_t last = sk_owner(s, tile_lo + s.k_iters - 1);
         out->contributors = (int32_t)(last - first + 1);
-        out->role = out->contributors == 1 ? ROLE_ONLY
-                    : (out->k_begin == 0 ? ROLE_STORER : ROLE_ADDER);
+        out->index = (int32_t)(v - first);
+        out->role = out->contributors == 1 ? ROLE_ONLY : ROLE_SHARED;
         return true;
       }
       b = lo;
@@ -126,8 +132,26 @@ G16_HD bool seg_at(const Sched& s, int32_t v, int32_t n, Segment* out) {
   out->k_begin = (int32_t)((int64_t)share * s.k_iters / splits);
   out->k_end = (int32_t)((int64_t)(share + 1) * s.k_iters / splits);
   out->contributors = splits;
-  out->role = splits == 1 ? ROLE_ONLY : (share == 0 ? ROLE_STORER : ROLE_ADDER);
+  out->index = share;
+  out->role = splits == 1 ? ROLE_ONLY : ROLE_SHARED;
   return true;
+}
+
+}  // namespace g16
+
+namespace g16 {
+
+// Most shares any tile has under schedule s (the workspace slots per tile).
+inline int32_t max_shares(const Sched& s) {
+  if (s.mode == MODE_SPLIT) return s.splits;
+  if (s.mode != MODE_STREAM_K) return 1;
+  int64_t most = 1;
+  for (int64_t t = 0; t < s.tiles; ++t) {
+    const int64_t lo = t * s.k_iters;
+    const int64_t c = sk_owner(s, lo + s.k_iters - 1) - sk_owner(s, lo) + 1;
+    if (c > most) most = c;
+  }
+  return (int32_t)most;
 }
 
 }  // namespace g16

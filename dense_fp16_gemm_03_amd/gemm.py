@@ -24,7 +24,7 @@ STATUS_NAMES = {
 EXPORTS = (
     "gemm_f16_f32_abt", "gemm_f16_f32_abt_workspace_size", "gemm_f16_f32_abt_ws",
     "gemm_status_string", "gemm_f16_f32_abt_describe", "gemm_f16_release_workspaces",
-    "gemm_f16_schedule_dump", "gemm_f16_wait_timeouts",
+    "gemm_f16_schedule_dump",
 )
 
 _lib = None
@@ -61,8 +61,6 @@ def load(path: str = LIBRARY):
     lib.gemm_f16_release_workspaces.restype = None
     lib.gemm_f16_schedule_dump.argtypes = [i64, i64, i64, i64, p, i64, p, p]
     lib.gemm_f16_schedule_dump.restype = i64
-    lib.gemm_f16_wait_timeouts.argtypes = []
-    lib.gemm_f16_wait_timeouts.restype = i64
     if path == LIBRARY:
         _lib = lib
     return lib
@@ -106,8 +104,8 @@ def gemm_f16_release_workspaces() -> None:
 
 
 def gemm_f16_schedule_dump(M, N, K, grid=0):
-    """(rows, k_iters, tiles): rows is a list of
-    (workgroup, tile, k_begin, k_end, role, contributors)."""
+    """(rows, k_iters, tiles): rows is an int64 array of
+    (workgroup, tile, k_begin, k_end, role, shares, index)."""
     import numpy as np
 
     lib = load()
@@ -115,14 +113,10 @@ def gemm_f16_schedule_dump(M, N, K, grid=0):
     n = lib.gemm_f16_schedule_dump(M, N, K, grid, None, 0, ctypes.byref(ki), ctypes.byref(nt))
     if n < 0:
         raise GemmError(1, "schedule_dump rejected the arguments")
-    out = np.zeros((max(n, 1), 6), dtype=np.int64)
+    out = np.zeros((max(n, 1), 7), dtype=np.int64)
     n2 = lib.gemm_f16_schedule_dump(M, N, K, grid, out.ctypes.data, n, None, None)
     assert n2 == n
     return out[:n], ki.value, nt.value
-
-
-def gemm_f16_wait_timeouts() -> int:
-    return load().gemm_f16_wait_timeouts()
 
 
 # --- torch convenience -----------------------------------------------------

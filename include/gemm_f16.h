@@ -46,9 +46,12 @@ typedef enum {
  * when M*N > 0 (A, B may be NULL when K = 0); C must not overlap A or B.
  * Any alignment of pointers and strides is accepted: 16-byte aligned A, B
  * with lda, ldb, K multiples of 8 take the tiled MFMA kernels, anything else
- * a slower general kernel. Split-K / stream-K plans use a workspace the
- * library allocates once per (device, stream) on first use; calls sharing a
- * stream are ordered by it, calls on different streams do not share one. */
+ * a slower general kernel. Split-K / stream-K plans write fp32 partial tiles
+ * to a workspace and a second kernel on the same stream sums them, in a fixed
+ * (k) order, into C, so results do not depend on timing. The workspace is
+ * library-owned, allocated once per (device, stream) on first use and grown
+ * when a larger one is needed; calls sharing a stream are ordered by it,
+ * calls on different streams do not share one. */
 gemm_status_t gemm_f16_f32_abt(int64_t M, int64_t N, int64_t K,
                                const void* A, int64_t lda,
                                const void* B, int64_t ldb,
@@ -58,11 +61,9 @@ gemm_status_t gemm_f16_f32_abt(int64_t M, int64_t N, int64_t K,
 size_t gemm_f16_f32_abt_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /* As gemm_f16_f32_abt, with a caller-owned device workspace of at least
- * gemm_f16_f32_abt_workspace_size(M, N, K) bytes, 256-byte aligned, which
- * must be zero-filled before its first use. The library leaves it zero-filled
- * again when each call's kernels finish, so it can be reused on the same
- * stream without clearing. Two calls in flight at once must not share it.
- * workspace may be NULL when the size is 0. */
+ * gemm_f16_f32_abt_workspace_size(M, N, K) bytes, 256-byte aligned. Its
+ * contents on entry do not matter. Two calls in flight at once must not share
+ * it. workspace may be NULL when the size is 0. */
 gemm_status_t gemm_f16_f32_abt_ws(int64_t M, int64_t N, int64_t K,
                                   const void* A, int64_t lda,
                                   const void* B, int64_t ldb,
@@ -81,22 +82,21 @@ gemm_status_t gemm_f16_f32_abt_describe(int64_t M, int64_t N, int64_t K, char* b
 void gemm_f16_release_workspaces(void);
 
 /* Host-side schedule model (no device is touched): fills out[] with one row
- * of 6 int64 per (workgroup, segment) of the persistent schedule for
- * (M, N, K) with `grid` workgroups (grid <= 0: the plan's own grid):
- *   { workgroup, tile, k_iter_begin, k_iter_end, role, contributors }
- * role 0 = only contributor (plain store), 1 = first k-share (plain store,
- * then raises the tile's flag), 2 = later k-share (waits, then adds).
+ * of 7 int64 per (workgroup, segment) of the persistent schedule for
+ * (M, N, K) with `grid` workgroups (grid <= 0: the plan's own grid; only
+ * stream-K and data-parallel plans accept another grid):
+ *   { workgroup, tile, k_iter_begin, k_iter_end, role, shares, index }
+ * role 0 = the tile's only unit (stores C directly); role 1 = one of `shares`
+ * units of a tile, `index` its position in k order (writes its partial tile
+ * to workspace slot `index`; the reduce kernel sums the slots into C).
  * Returns the number of rows (writes at most `cap`), or -1 on bad arguments.
  * *k_iters and *tiles (if non-NULL) receive the plan's k-iterations per tile
  * and its output-tile count. Used by tests to check that every (tile, k-iter)
- * is covered exactly once and every shared tile has exactly one storer. */
+ * is covered exactly once and that the shares of a tile are numbered 0..s-1
+ * in k order. */
 int64_t gemm_f16_schedule_dump(int64_t M, int64_t N, int64_t K, int64_t grid,
                                int64_t* out, int64_t cap, int64_t* k_iters, int64_t* tiles);
 
-/* Number of flag waits that gave up after the bounded spin, summed over the
- * library-owned workspaces of the current device (synchronises them). A
- * non-zero value means a result computed during that time may be wrong. */
-int64_t gemm_f16_wait_timeouts(void);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = header_functions()
-    assert len(names) >= 8
+    assert len(names) >= 7
     for name in names:
         assert hasattr(lib, name), f"{name} declared in gemm_f16.h but not exported"
     assert sorted(gemm.EXPORTS) == names
@@ -98,34 +98,34 @@ def test_describe_general_and_empty(lib):
 # --- schedule model ----------------------------------------------------------
 
 def check_schedule(rows, k_iters, tiles):
-    """Every (tile, k-iteration) covered exactly once; a tile split among
-    several segments has exactly one storer (role 1) holding k = 0, the rest
-    adders (role 2); a whole tile is role 0; contributors == segment count."""
+    """Every (tile, k-iteration) covered exactly once. A tile covered by one
+    segment has role 0; a tile split among s segments has them all role 1,
+    numbered 0..s-1 in increasing k, each reporting shares == s."""
     errors = []
     cover = np.zeros((tiles, k_iters), dtype=np.int64)
     per_tile = {}
-    for w, t, kb, ke, role, contrib in rows:
+    for w, t, kb, ke, role, shares, index in rows:
         if not (0 <= t < tiles and 0 <= kb < ke <= k_iters):
             errors.append(f"bad segment {(w, t, kb, ke)}")
             continue
         cover[t, kb:ke] += 1
-        per_tile.setdefault(t, []).append((kb, ke, role, contrib))
+        per_tile.setdefault(t, []).append((kb, ke, role, shares, index))
     if not np.all(cover == 1):
         bad = np.argwhere(cover != 1)[:3]
         errors.append(f"coverage != 1 at (tile, k) {bad.tolist()}")
     for t, segs in per_tile.items():
         n = len(segs)
-        if any(c != n for _, _, _, c in segs):
-            errors.append(f"tile {t}: contributors field != {n}")
-        roles = sorted(r for _, _, r, _ in segs)
-        if n == 1 and roles != [0]:
-            errors.append(f"tile {t}: single segment with role {roles}")
-        if n > 1:
-            if roles != [1] + [2] * (n - 1):
-                errors.append(f"tile {t}: roles {roles}")
-            storer = [s for s in segs if s[2] == 1]
-            if storer and storer[0][0] != 0:
-                errors.append(f"tile {t}: storer does not hold k = 0")
+        if any(sh != n for _, _, _, sh, _ in segs):
+            errors.append(f"tile {t}: shares field != {n}")
+        if n == 1:
+            if segs[0][2] != 0:
+                errors.append(f"tile {t}: single segment with role {segs[0][2]}")
+            continue
+        if any(r != 1 for _, _, r, _, _ in segs):
+            errors.append(f"tile {t}: shared tile with a role other than 1")
+        by_k = sorted(segs)
+        if [ix for *_, ix in by_k] != list(range(n)):
+            errors.append(f"tile {t}: share indices {[ix for *_, ix in by_k]} not 0..{n - 1} in k order")
     if len(per_tile) != tiles:
         errors.append(f"{tiles - len(per_tile)} tiles never scheduled")
     return errors
@@ -142,6 +142,7 @@ SCHED_CASES = [
     (1000, 1500, 4104, "mode=2,grid=200"),
     (777, 333, 1000, "mode=2,kid=4,grid=77"),
     (5000, 300, 2048, "mode=1,splits=3"),
+    (5000, 300, 2048, "mode=1,splits=3,grid=50"),   # split-K over several rounds
     (3000, 2900, 1024, None),
 ]
 
@@ -169,21 +170,18 @@ def test_schedule_model_detects_dropped_unit(lib, monkeypatch, M, N, K, plan):
         assert check_schedule(rows + [rows[i]], k_iters, tiles) != []
 
 
-def test_stream_k_storer_segment_first(lib, monkeypatch):
-    """In stream-K a workgroup walks its range from the end, so a segment that
-    starts a tile (and stores it) never comes after a segment that waits."""
-    monkeypatch.setenv("GEMM_F16_PLAN", "mode=2,grid=200")
-    rows, _, _ = gemm.gemm_f16_schedule_dump(1000, 1500, 4104)
-    by_wg = {}
-    for w, t, kb, ke, role, c in rows.tolist():
-        by_wg.setdefault(w, []).append(role)
-    for w, roles in by_wg.items():
-        if 2 in roles:
-            assert roles.index(2) == len(roles) - 1, f"workgroup {w} waits before storing"
+def test_planted_index_error_detected(lib, monkeypatch):
+    """Swapping two shares' indices must fail the model (k order matters)."""
+    rows, k_iters, tiles = gemm.gemm_f16_schedule_dump(1024, 1024, 65536)
+    rows = rows.tolist()
+    a = next(i for i, r in enumerate(rows) if r[4] == 1 and r[6] == 0)
+    b = next(i for i, r in enumerate(rows) if r[1] == rows[a][1] and r[6] == 1)
+    rows[a][6], rows[b][6] = rows[b][6], rows[a][6]
+    assert check_schedule(rows, k_iters, tiles) != []
 
 
-def test_grid_fits_one_workgroup_per_cu(lib):
-    """Split / stream-K plans wait on flags: their grid must be co-resident."""
+def test_default_plans(lib):
+    """The five workloads take the tiled kernels with at most 256 workgroups."""
     for M, N, K in inputs.WORKLOADS.values():
         rows, _, _ = gemm.gemm_f16_schedule_dump(M, N, K)
         assert rows[:, 0].max() < 256

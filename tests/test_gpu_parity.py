@@ -247,10 +247,11 @@ def test_subnormal_inputs():
 
 # --- every kernel variant and schedule mode ---------------------------------
 
-PLANS = [f"kid={k}" for k in range(7)] + [
+PLANS = [f"kid={k}" for k in range(10)] + [
     "kid=0,mode=1,splits=3", "kid=0,mode=2", "kid=0,mode=2,grid=37",
     "kid=4,mode=2,grid=100", "kid=6,mode=1,splits=5", "kid=2,mode=2,grid=64",
     "kid=1,mode=1,splits=2", "kid=3,mode=2,grid=29", "kid=5,mode=2,grid=130",
+    "kid=7,mode=1,splits=4", "kid=9,mode=2", "kid=4,mode=1,splits=3,grid=40",
 ]
 
 
@@ -281,22 +282,21 @@ def test_transpose_invariant():
 
 
 @pytest.mark.parametrize("name", ["2048x2048x16384", "1024x1024x65536"])
-def test_repeat_and_workspace_returns_to_zero(name):
-    """Two calls give identical integer results (flags/counters left clean),
-    and a caller workspace is zero again after each call."""
+def test_repeat_and_caller_workspace(name):
+    """Split-K / stream-K results are bitwise repeatable (partials are summed in
+    k order), also on uniform inputs, and a caller workspace holding garbage
+    gives the same C."""
     M, N, K = WORKLOADS[name]
-    A, B = operands((M, N, K), "integer")
+    A, B = operands((M, N, K), "uniform")
     At, Bt = to_dev(A), to_dev(B)
     first = run(At, Bt)
     second = run(At, Bt, fill=-7.0)
     assert np.array_equal(first, second)
     nbytes = gemm.gemm_f16_f32_abt_workspace_size(M, N, K)
     assert nbytes > 0
-    ws = torch.zeros(nbytes // 4, dtype=torch.int32, device=DEV)
+    ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device=DEV)
     for _ in range(2):
-        third = run(At, Bt, workspace=ws)
-        assert np.array_equal(first, third)
-        assert int(ws.count_nonzero().item()) == 0, "workspace not zero after the call"
+        assert np.array_equal(first, run(At, Bt, workspace=ws))
 
 
 def test_non_default_stream():
@@ -311,7 +311,3 @@ def test_non_default_stream():
         gemm.gemm_abt(At, Bt, C)
     s.synchronize()
     assert np.array_equal(C.cpu().numpy(), ref)
-
-
-def test_no_flag_wait_gave_up():
-    assert gemm.gemm_f16_wait_timeouts() == 0
