@@ -19,6 +19,8 @@ namespace {
 using namespace g16;
 
 constexpr int32_t kDefaultCUs = 256;  // MI355X: 8 XCDs x 32 CUs
+// Kernel for large squares (one 256x256 tile or more per CU).
+constexpr int32_t KID_LARGE = KID_256x256x32_S5_W4;
 
 struct Plan {
   int32_t kid = -1;       // tiled kernel id, KID_GENERAL, or -1 (nothing to do)
@@ -100,12 +102,14 @@ bool tiled_eligible(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
 
 // Shape -> kernel and schedule. The pages' rule (section "Inside the kernels"
 // of "SASS-Level Kernel Generation for Blackwell") picks per shape a tile, a
-// ring depth and how K is divided; this is the same kind of rule for 256 CUs:
-//   * enough 256x256 tiles to fill the CUs: 256x256, data-parallel,
+// ring depth and how K is divided; this is the same kind of rule for 256 CUs,
+// set from measurements on the MI355X:
+//   * at least one 256x256 tile per CU: 256x256 tiles, data-parallel,
 //     persistent grid walking the tiles by stride;
-//   * few tiles but long K: 256x256 with K split so tiles x splits fills
-//     the CUs (each share keeps >= 8 k-iterations);
-//   * small problems: smaller tiles, split K a little if K allows.
+//   * fewer tiles but long K (>= 64 k-steps of 64): 256x128 tiles with K
+//     split so tiles x splits fills the CUs (each share keeps >= 8 k-steps);
+//   * small problems: 128x128 tiles (64x64 when there are fewer than 16 of
+//     them), data-parallel; the splits' reduce pass costs more than it gains.
 Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                int64_t ldb, const float* C, int64_t ldc, int32_t cus) {
   Plan plan;
@@ -113,34 +117,23 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
   plan.c_vec4 = ((uintptr_t)C % 16 == 0) && (ldc % 4 == 0);
   const Override o = read_override();
 
-  int32_t kid = KID_256x256x64_S2_W4;
+  int32_t kid = KID_LARGE;
   int32_t mode = MODE_DATA_PARALLEL;
   int32_t splits = 1;
   {
     const int64_t t256 = cdiv(M, 256) * cdiv(N, 256);
     const int64_t k64 = cdiv(K, 64);
     if (t256 >= cus) {
-      kid = KID_256x256x64_S2_W4;
-    } else if (t256 * k64 >= (int64_t)cus * 32) {
-      kid = KID_256x256x64_S2_W4;
-      splits = (int32_t)(cus / t256);
-      if (splits > k64 / 8) splits = (int32_t)(k64 / 8);
+      kid = KID_LARGE;
+    } else if (k64 >= 64) {
+      kid = KID_256x128x64_S3_W4;
+      const int64_t tiles = cdiv(M, 256) * cdiv(N, 128);
+      int64_t sp = tiles >= cus ? 1 : cus / tiles;
+      if (sp > k64 / 8) sp = k64 / 8;
+      splits = (int32_t)std::max<int64_t>(sp, 1);
       mode = splits > 1 ? MODE_SPLIT : MODE_DATA_PARALLEL;
     } else {
-      const int64_t t128 = cdiv(M, 128) * cdiv(N, 128);
-      if (t128 * 4 >= cus || cdiv(M, 64) * cdiv(N, 64) < cus / 2) {
-        kid = t128 >= 16 ? KID_128x128x64_S4_W4 : KID_64x64x64_S4_W4;
-      } else {
-        kid = KID_64x64x64_S4_W4;
-      }
-      const KernelInfo* ki = kernel_info(kid);
-      const int64_t tiles = cdiv(M, ki->bm) * cdiv(N, ki->bn);
-      const int64_t kits = cdiv(K, ki->bk);
-      int64_t sp = tiles >= cus ? 1 : cus / tiles;
-      if (sp > kits / 4) sp = kits / 4;
-      if (sp < 1) sp = 1;
-      splits = (int32_t)sp;
-      mode = splits > 1 ? MODE_SPLIT : MODE_DATA_PARALLEL;
+      kid = cdiv(M, 128) * cdiv(N, 128) >= 16 ? KID_128x128x64_S4_W4 : KID_64x64x64_S4_W4;
     }
   }
   if (o.kid >= 0 && kernel_info(o.kid)) kid = o.kid;
