@@ -2,7 +2,7 @@
 """Benchmark of C = A * B^T (fp16 in, fp32 accumulate/out) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8192^3]
-                    [--no-cpu-baseline] [--shapes] [--calibrate-copy]
+                    [--no-cpu-baseline] [--shapes] [--vendor] [--calibrate-copy]
 
 A step is one call of gemm_f16_f32_abt through the C ABI on synthetic
 operands already resident in HBM (uniform [-1, 1] fp16, seeds 1 and 2). The
@@ -129,6 +129,106 @@ def cpu_baseline(A, B, M, N, K, budget_s=10.0):
                       f"binary64 triple loop on {threads} threads"}
 
 
+def _time_alone(torch, fn, calls, warmup=5):
+    """Median GPU time (us) of fn() when every call runs alone."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = []
+    for _ in range(calls):
+        s.record(stream)
+        fn()
+        e.record(stream)
+        e.synchronize()
+        out.append(s.elapsed_time(e) * 1e3)
+    out.sort()
+    return out[len(out) // 2]
+
+
+def vendor_arm(torch, gemm, names, dev):
+    """hipBLASLt context arm ("How we measured" in "SASS-Level Kernel
+    Generation for Blackwell"): every algorithm of the vendor heuristic is run
+    on hash-integer inputs, where any summation order is exact, and kept only
+    if its C equals ours bit for bit; the fastest kept one is then timed
+    against ours, calls alone, in the order ours, vendor, vendor, ours, on
+    both uniform and hash-integer inputs. Context only, never the bench value."""
+    import ctypes
+
+    from dense_fp16_gemm_03_amd import build as b
+    from dense_fp16_gemm_03_amd import inputs
+
+    if not os.path.exists(b.VENDOR_LIBRARY):
+        raise RuntimeError(f"{b.VENDOR_LIBRARY} is not built "
+                           "(python -m dense_fp16_gemm_03_amd.build --vendor)")
+    lib = ctypes.CDLL(b.VENDOR_LIBRARY)
+    i64, p = ctypes.c_int64, ctypes.c_void_p
+    lib.vendor_hipblaslt_prepare.argtypes = [i64] * 7
+    lib.vendor_hipblaslt_prepare.restype = i64
+    lib.vendor_hipblaslt_workspace.argtypes = [i64]
+    lib.vendor_hipblaslt_workspace.restype = ctypes.c_size_t
+    lib.vendor_hipblaslt_run.argtypes = [i64, p, p, p, p, ctypes.c_size_t, p]
+    lib.vendor_hipblaslt_run.restype = ctypes.c_int
+    out = []
+    for n in names:
+        M, N, K = inputs.WORKLOADS[n]
+        count = lib.vendor_hipblaslt_prepare(M, N, K, K, K, N, 64)
+        if count <= 0:
+            log(f"[vendor] {n}: heuristic returned {count}")
+            out.append({"workload": n, "algorithms": int(count)})
+            continue
+        ws_bytes = max(lib.vendor_hipblaslt_workspace(i) for i in range(count))
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        stream = torch.cuda.current_stream().cuda_stream
+        Ch = torch.empty((M, N), dtype=torch.float32, device=dev)
+        Cv = torch.empty_like(Ch)
+        Ah, Bh = (torch.from_numpy(x).to(dev) for x in inputs.workload_operands((M, N, K),
+                                                                                 "hash_int"))
+        gemm.gemm_abt(Ah, Bh, Ch)
+
+        def run_vendor(i, A_, B_, C_):
+            st = lib.vendor_hipblaslt_run(i, A_.data_ptr(), B_.data_ptr(), C_.data_ptr(),
+                                          ws.data_ptr(), ws.numel(), stream)
+            if st != 0:
+                raise RuntimeError(f"hipBLASLt algorithm {i} failed with status {st}")
+
+        screen_calls = 10 if M * N * K >= 1 << 36 else 50
+        exact, times = 0, []
+        for i in range(count):
+            Cv.fill_(float("nan"))
+            run_vendor(i, Ah, Bh, Cv)
+            torch.cuda.synchronize()
+            if not torch.equal(Cv, Ch):
+                continue
+            exact += 1
+            times.append((_time_alone(torch, lambda: run_vendor(i, Ah, Bh, Cv), screen_calls), i))
+        if not times:
+            out.append({"workload": n, "algorithms": int(count), "exact": 0})
+            continue
+        best = min(times)[1]
+        entry = {"workload": n, "M": M, "N": N, "K": K, "algorithms": int(count),
+                 "exact": exact, "best_algorithm": best}
+        for kind, (A_, B_) in (("uniform", make_device_operands(torch, (M, N, K), dev)[2:]),
+                               ("hash_int", (Ah, Bh))):
+            ours, theirs = [], []
+            for who in ("ours", "vendor", "vendor", "ours"):
+                if who == "ours":
+                    ours.append(_time_alone(torch, lambda: gemm.gemm_abt(A_, B_, Ch), CALLS[n]))
+                else:
+                    theirs.append(_time_alone(torch, lambda: run_vendor(best, A_, B_, Cv),
+                                              CALLS[n]))
+            entry[kind] = {"ours_us": [round(min(ours), 3), round(max(ours), 3)],
+                           "hipblaslt_us": [round(min(theirs), 3), round(max(theirs), 3)]}
+            log(f"[vendor] {n} {kind}: ours {min(ours):.2f}-{max(ours):.2f} us, hipBLASLt "
+                f"{min(theirs):.2f}-{max(theirs):.2f} us (algorithm {best} of {count}, "
+                f"{exact} exact)")
+        out.append(entry)
+        del Ah, Bh, Ch, Cv, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def calibrate_copy(torch):
     """A plain copy of known size for scaling the HBM byte counters:
     1 GiB fp32 read + 1 GiB written per launch (torch's elementwise kernel)."""
@@ -167,6 +267,9 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB fp32 copy kernel (counter calibration)")
     ap.add_argument("--sweeps", type=int, default=2, help="forward/reverse sweeps for shapes")
+    ap.add_argument("--vendor", action="store_true",
+                    help="also time hipBLASLt's fastest exact algorithm on every workload "
+                         "(context only)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -244,6 +347,10 @@ def main():
                 entry["pages_b200_us"] = PAGE_US[n]
             shapes.append(entry)
 
+    vendor = None
+    if args.vendor:
+        vendor = vendor_arm(torch, gemm, list(inputs.WORKLOADS), dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU reference on a sample ...")
@@ -264,6 +371,8 @@ def main():
                    "source_hash": source_hash()},
         "roofline": roofline, "cpu_baseline": cpu, "shapes": shapes,
     }
+    if vendor is not None:
+        line["vendor_hipblaslt"] = vendor
     print(json.dumps(line), flush=True)
 
 

@@ -1,9 +1,10 @@
 """Build libgemm_f16.so (hipcc, gfx950) in the package directory.
 
-    python -m dense_fp16_gemm_03_amd.build [--asm]
+    python -m dense_fp16_gemm_03_amd.build [--asm] [--vendor]
 
 ``--asm`` also writes the gfx950 assembly of the kernels to ``_build/`` so
-register, spill and LDS figures can be read from it.
+register, spill and LDS figures can be read from it. ``--vendor`` also builds
+libvendor_hipblaslt.so, the hipBLASLt context arm bench.py --vendor times.
 """
 from __future__ import annotations
 
@@ -19,6 +20,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libgemm_f16.so")
 ASM_DIR = os.path.join(ROOT, "_build")
 SOURCES = [os.path.join(CSRC, "gemm_kernels.hip"), os.path.join(CSRC, "gemm_api.cpp")]
+# hipBLASLt context arm (measurement only; see vendor/hipblaslt_arm.cpp).
+VENDOR_SOURCE = os.path.join(PKG, "vendor", "hipblaslt_arm.cpp")
+VENDOR_LIBRARY = os.path.join(PKG, "libvendor_hipblaslt.so")
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are kept out of the generated code (this flag is a
@@ -50,6 +54,19 @@ def build(asm: bool = False, verbose: bool = False) -> str:
     return LIBRARY
 
 
+def build_vendor(verbose: bool = False) -> str:
+    """The hipBLASLt context arm: host code only, linked against hipBLASLt."""
+    tmp = VENDOR_LIBRARY + ".tmp"
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = [hipcc(), "-O2", "-std=c++17", "-fPIC", "-shared", VENDOR_SOURCE,
+           f"-L{rocm}/lib", "-lhipblaslt", f"-Wl,-rpath,{rocm}/lib", "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, VENDOR_LIBRARY)
+    return VENDOR_LIBRARY
+
+
 def emit_asm(verbose: bool = False) -> str:
     """Device assembly of the kernels (gfx950) into _build/gemm_kernels-gfx950.s."""
     os.makedirs(ASM_DIR, exist_ok=True)
@@ -64,3 +81,5 @@ def emit_asm(verbose: bool = False) -> str:
 if __name__ == "__main__":
     build(asm="--asm" in sys.argv, verbose=True)
     print(LIBRARY)
+    if "--vendor" in sys.argv:
+        print(build_vendor(verbose=True))

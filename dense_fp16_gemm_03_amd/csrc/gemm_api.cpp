@@ -19,8 +19,11 @@ namespace {
 using namespace g16;
 
 constexpr int32_t kDefaultCUs = 256;  // MI355X: 8 XCDs x 32 CUs
-// Kernel for large squares (one 256x256 tile or more per CU).
-constexpr int32_t KID_LARGE = KID_256x256x32_S5_W4;
+// Kernel for large squares (one 256x256 tile or more per CU): 16x16x32 MFMA,
+// two waves per SIMD, fragment reads placed after their last use.
+constexpr int32_t KID_LARGE = KID_256x256x32_S5_W8_M16_RS;
+// Kernel for long-K shapes with fewer 256x256 tiles than CUs.
+constexpr int32_t KID_LONG_K = KID_256x128x64_S3_W4_M16;
 
 struct Plan {
   int32_t kid = -1;       // tiled kernel id, KID_GENERAL, or -1 (nothing to do)
@@ -126,7 +129,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
     if (t256 >= cus) {
       kid = KID_LARGE;
     } else if (k64 >= 64) {
-      kid = KID_256x128x64_S3_W4;
+      kid = KID_LONG_K;
       const int64_t tiles = cdiv(M, 256) * cdiv(N, 128);
       int64_t sp = tiles >= cus ? 1 : cus / tiles;
       if (sp > k64 / 8) sp = k64 / 8;

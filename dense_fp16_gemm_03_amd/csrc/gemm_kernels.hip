@@ -13,22 +13,22 @@
 //     flight while iteration i computes; a wait on the load counter plus a
 //     workgroup barrier hands a stage over, and the tail waits on fewer loads
 //     when no more are issued (the "commit empty groups" rule of that page).
-//   * LDS -> registers with ds_read_b128 (8 halves a lane) and
-//     v_mfma_f32_32x32x16_f16 into per-wave register-blocked accumulators.
-//     The next stage is handed over before the last k-step's MFMAs are issued,
-//     so its first fragments load while those MFMAs run ("asking a stage
-//     ahead" in "SASS-Level Kernel Generation for Blackwell", section "Inside
-//     the kernels").
+//   * LDS -> registers with ds_read_b128 (8 halves a lane) and an fp16 MFMA
+//     (v_mfma_f32_32x32x16_f16 or v_mfma_f32_16x16x32_f16) into per-wave
+//     register-blocked accumulators. The next stage is handed over before the
+//     last k-step's MFMAs are issued, so its first fragments load while those
+//     MFMAs run ("asking a stage ahead" in "SASS-Level Kernel Generation for
+//     Blackwell", section "Inside the kernels").
 //   * the B tile is fed as the MFMA's first operand and the A tile as its
 //     second (SwapAB in the same section), so each lane ends up holding runs
 //     of 4 consecutive columns of C and stores them as one 16-byte write,
 //     straight from the registers ("stored from the registers").
-//   * split-K / stream-K: the share holding a tile's first k-iteration stores
-//     the tile and raises the tile's flag; every other share waits for the
-//     flag and adds its partial sums with fp32 atomics at device scope
-//     (section "Inside the kernels", "Stream-K and split-K, added in the L2").
-//     The last adder puts the flag and arrival count back to zero, so the
-//     workspace is zero whenever no call is running.
+//   * split-K / stream-K (section "Inside the kernels", where the shares of a
+//     tile are added in the L2): a tile whose k-iterations are shared among
+//     workgroups is not added in place. Every share writes its fp32 partial
+//     tile to a workspace slot, and a reduce kernel that follows on the same
+//     stream sums the slots of each tile in k order and writes C, so the
+//     result does not depend on timing and needs no flags or atomics.
 #include "gemm_kernels.h"
 
 #include <hip/hip_runtime.h>
@@ -50,15 +50,66 @@ constexpr int32_t kNumRecords = 0x7FFFFFF0;
 constexpr int32_t kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kReduceThreads = 256;
 
-template <int BM_, int BN_, int BK_, int STAGES_, int WGM_, int WGN_>
+// The two fp16 MFMA shapes with fp32 accumulation on gfx950. Both take 8
+// halves of each operand per lane; the B tile is the first operand and the A
+// tile the second (SwapAB), so a block's accumulators run along N.
+//   32x32x16: operand lane l holds row l % 32, k = 8 (l / 32) .. +7 of the
+//     k-step; accumulator register 4g + q of lane l is row (m) l % 32,
+//     column (n) 8g + 4 (l / 32) + q of the block.
+//   16x16x32: operand lane l holds row l % 16, k = 8 (l / 16) .. +7;
+//     accumulator register q of lane l is row l % 16, column 4 (l / 16) + q.
+// On random data the 16x16x32 form reaches a higher sustained clock under
+// the board's power limit, for the same work.
+template <int MI>
+struct Mma;
+
+template <>
+struct Mma<32> {
+  static constexpr int DIM = 32;    // rows (and columns) of an accumulator block
+  static constexpr int KW = 16;     // k per instruction
+  static constexpr int GROUPS = 4;  // runs of 4 consecutive columns per lane
+  typedef f32x16 acc_t;
+  static __device__ __forceinline__ acc_t mma(half8 b, half8 a, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ int frag_row(int lane) { return lane & 31; }
+  static __device__ __forceinline__ int frag_chunk(int ks, int lane) { return 2 * ks + (lane >> 5); }
+  static __device__ __forceinline__ int acc_m(int lane) { return lane & 31; }
+  static __device__ __forceinline__ int acc_n(int g, int lane) { return 8 * g + 4 * (lane >> 5); }
+};
+
+template <>
+struct Mma<16> {
+  static constexpr int DIM = 16;
+  static constexpr int KW = 32;
+  static constexpr int GROUPS = 1;
+  typedef f32x4 acc_t;
+  static __device__ __forceinline__ acc_t mma(half8 b, half8 a, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ int frag_row(int lane) { return lane & 15; }
+  static __device__ __forceinline__ int frag_chunk(int ks, int lane) { return 4 * ks + (lane >> 4); }
+  static __device__ __forceinline__ int acc_m(int lane) { return lane & 15; }
+  static __device__ __forceinline__ int acc_n(int, int lane) { return 4 * (lane >> 4); }
+};
+
+// RS_: when the fragment reads of the next k-step are issued. 0: spread
+// evenly over the k-step's MFMAs; 1: each right after the last MFMA that uses
+// the fragment it replaces, so the current and next fragments barely overlap
+// in registers (for register-bound variants).
+template <int BM_, int BN_, int BK_, int STAGES_, int WGM_, int WGN_, int MI_ = 32, int RS_ = 0>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
   static constexpr int WGM = WGM_, WGN = WGN_;
+  static constexpr int MI = MI_;
+  static constexpr int RS = RS_;
+  using M = Mma<MI>;
+  using acc_t = typename M::acc_t;
   static constexpr int WAVES = WGM * WGN;
   static constexpr int THREADS = WAVES * 64;
   static constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
-  static constexpr int FM = WM / 32, FN = WN / 32;    // 32x32 MFMA blocks per wave
-  static constexpr int KSTEPS = BK / 16;              // MFMA k-steps per stage
+  static constexpr int FM = WM / M::DIM, FN = WN / M::DIM;  // MFMA blocks per wave
+  static constexpr int KSTEPS = BK / M::KW;                 // MFMA k-steps per stage
   static constexpr int ROW_BYTES = BK * 2;
   static constexpr int CHUNKS = BK / 8;               // 16-byte chunks per tile row
   static constexpr int RPL = 64 / CHUNKS;             // tile rows per 1 KiB wave load
@@ -70,7 +121,8 @@ struct Cfg {
   static constexpr int B_LOADS = BN / RPL / WAVES;
   static constexpr int LOADS = A_LOADS + B_LOADS;
   static constexpr int WAVES_PER_EU = WAVES / 4;
-  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 blocks");
+  static_assert(WM % M::DIM == 0 && WN % M::DIM == 0, "wave tile must be whole MFMA blocks");
+  static_assert(KSTEPS >= 1, "a stage holds at least one k-step");
   static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
   static_assert(A_LOADS >= 1 && B_LOADS >= 1, "every wave loads A and B");
   static_assert(A_LOADS * RPL * WAVES == BM && B_LOADS * RPL * WAVES == BN, "load split");
@@ -80,17 +132,26 @@ struct Cfg {
 };
 
 // Position of logical 16-byte chunk `chunk` of tile row `row` inside the row.
-// CHUNKS == 8: f(row) = (row ^ (row >> 3)) & 7. Any 8 consecutive rows get
-// distinct f, and so do the 8 even (and the 8 odd) rows of any 16 aligned
-// rows, so the 8- and 16-lane phases of a ds_read_b128 fragment read (lanes
-// on consecutive rows, one chunk) never meet in a bank.
-// CHUNKS == 4: the same property for 64-byte rows with f in 0..3.
-template <int CHUNKS>
+// A fragment read puts lane l on row l % DIM, chunk l / DIM of its k-step
+// (DIM = 32 or 16, the MFMA block height). On gfx950 the LDS serves a
+// ds_read_b128 in four passes of 16 lanes, and the passes are not runs of
+// consecutive lanes: measured, one pass holds lanes 0-3, 12-15, 20-23 and
+// 24-27, another 4-11, 16-19 and 28-31 (and the same two sets shifted by
+// 32). With 64 banks of 4 bytes a pass is conflict-free when its 16 lanes
+// land in 16 different 16-byte bank groups; each f below is one-to-one where
+// that requires it (checked exhaustively for every pass, k-step and block row).
+//   DIM 32, 128-byte rows: f = (row ^ (row >> 3)) & 7
+//   DIM 32,  64-byte rows: f = (row >> 2) & 3
+//   DIM 16, 128-byte rows: f = (row >> 1) & 7
+//   DIM 16,  64-byte rows: f = ((row >> 2) ^ ((row >> 1) & 2)) & 3
+template <int CHUNKS, int DIM>
 __device__ __forceinline__ int swz(int row, int chunk) {
-  if constexpr (CHUNKS == 8) {
-    return chunk ^ ((row ^ (row >> 3)) & 7);
+  if constexpr (DIM == 32) {
+    if constexpr (CHUNKS == 8) return chunk ^ ((row ^ (row >> 3)) & 7);
+    else return chunk ^ ((row >> 2) & 3);
   } else {
-    return chunk ^ (((row >> 1) ^ (row >> 3)) & 3);
+    if constexpr (CHUNKS == 8) return chunk ^ ((row >> 1) & 7);
+    else return chunk ^ (((row >> 2) ^ ((row >> 1) & 2)) & 3);
   }
 }
 
@@ -123,27 +184,25 @@ struct Frags {
   half8 b[C::FN];
 };
 
-// Per-lane LDS byte offsets of the fragments of k-step ks (relative to a stage).
-// A fragment fm: rows wm*WM + fm*32 + lane%32, k = 16*ks + 8*(lane/32) .. +7.
+// Per-lane LDS byte offset (relative to a stage) of the fragment of k-step
+// ks whose block starts at tile row `block_row`.
 template <class C>
-__device__ __forceinline__ int frag_off(int tile_row, int ks, int lane) {
-  const int c = 2 * ks + (lane >> 5);
-  return tile_row * C::ROW_BYTES + swz<C::CHUNKS>(tile_row, c) * 16;
+__device__ __forceinline__ int frag_off(int block_row, int ks, int lane) {
+  const int row = block_row + C::M::frag_row(lane);
+  return row * C::ROW_BYTES + swz<C::CHUNKS, C::M::DIM>(row, C::M::frag_chunk(ks, lane)) * 16;
 }
 
 template <class C>
 __device__ __forceinline__ void read_frags(const char* stage, int ks, int wm, int wn, int lane,
                                            Frags<C>& f) {
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-    const int row = wm * C::WM + i * 32 + (lane & 31);
-    f.a[i] = *reinterpret_cast<const half8*>(stage + frag_off<C>(row, ks, lane));
-  }
+  for (int i = 0; i < C::FM; ++i)
+    f.a[i] = *reinterpret_cast<const half8*>(
+        stage + frag_off<C>(wm * C::WM + i * C::M::DIM, ks, lane));
 #pragma unroll
-  for (int j = 0; j < C::FN; ++j) {
-    const int row = wn * C::WN + j * 32 + (lane & 31);
-    f.b[j] = *reinterpret_cast<const half8*>(stage + C::A_BYTES + frag_off<C>(row, ks, lane));
-  }
+  for (int j = 0; j < C::FN; ++j)
+    f.b[j] = *reinterpret_cast<const half8*>(
+        stage + C::A_BYTES + frag_off<C>(wn * C::WN + j * C::M::DIM, ks, lane));
 }
 
 // Buffer offsets (bytes, relative to the tile's first row at k = 0) of this
@@ -164,7 +223,7 @@ __device__ __forceinline__ void make_load_map(LoadMap<C, LOADS_OF>& m, int wave,
   for (int j = 0; j < LOADS_OF; ++j) {
     const int group = wave * LOADS_OF + j;
     const int row = group * C::RPL + lane / C::CHUNKS;
-    const int chunk = swz<C::CHUNKS>(row, lane % C::CHUNKS);  // XOR: its own inverse
+    const int chunk = swz<C::CHUNKS, C::M::DIM>(row, lane % C::CHUNKS);  // XOR: own inverse
     m.off[j] = row < rows_valid ? (uint32_t)(row * ld * 2 + chunk * 16) : kMaskedOffset;
     m.lim[j] = k_limit - chunk * 8;
   }
@@ -193,23 +252,115 @@ __device__ __forceinline__ void issue_one(int j, char* dst, const Operands& op,
   }
 }
 
-// How many of n items spread evenly over nm MFMAs fall after MFMA m.
+// Items spread evenly over nm MFMAs: item r goes after MFMA r * nm / n.
+// items_at: how many go after MFMA m; items_before: how many before it.
 constexpr int items_at(int n, int nm, int m) {
   int c = 0;
   for (int r = 0; r < n; ++r) c += (r * nm / n == m);
   return c;
 }
+constexpr int items_before(int n, int nm, int m) {
+  int c = 0;
+  for (int r = 0; r < n; ++r) c += (r * nm / n < m);
+  return c;
+}
+
+// Fragment reads of the next k-step, in issue order r = 0 .. FM + FN - 1.
+// MFMAs run row by row (block (i, j) is MFMA i * FN + j), so A fragment i is
+// last used by MFMA i * FN + FN - 1 and B fragment j by (FM - 1) * FN + j.
+//   RS 0: read r is A fragment r (r < FM), else B fragment r - FM, issued
+//         after MFMA r * NM / NR.
+//   RS 1: A fragments 0 .. FM - 2, then the B fragments, then A fragment
+//         FM - 1, each issued after the last use of the one it replaces.
+// read_frag(r): fragment id (A i -> i, B j -> FM + j); read_slot(r): MFMA.
+constexpr int read_frag(int rs, int fm, int fn, int r) {
+  if (rs == 0) return r;
+  if (r < fm - 1) return r;
+  if (r < fm - 1 + fn) return fm + (r - (fm - 1));
+  return fm - 1;
+}
+constexpr int read_slot(int rs, int fm, int fn, int r) {
+  const int nm = fm * fn, nr = fm + fn;
+  if (rs == 0) return r * nm / nr;
+  const int f = read_frag(rs, fm, fn, r);
+  return f < fm ? f * fn + fn - 1 : (fm - 1) * fn + (f - fm);
+}
+constexpr int reads_at(int rs, int fm, int fn, int m) {
+  int c = 0;
+  for (int r = 0; r < fm + fn; ++r) c += (read_slot(rs, fm, fn, r) == m);
+  return c;
+}
+constexpr int reads_before(int rs, int fm, int fn, int m) {
+  int c = 0;
+  for (int r = 0; r < fm + fn; ++r) c += (read_slot(rs, fm, fn, r) < m);
+  return c;
+}
+constexpr bool read_slots_sorted(int rs, int fm, int fn) {
+  for (int r = 1; r < fm + fn; ++r)
+    if (read_slot(rs, fm, fn, r) < read_slot(rs, fm, fn, r - 1)) return false;
+  return true;
+}
 
 // Scheduling groups for one k-step: MFMA m, then its reads, then its loads.
-template <int NM, int NR, int NL, int M>
+template <class C, int NL, int M>
 __device__ __forceinline__ void sched_pattern() {
+  constexpr int NM = C::FM * C::FN;
   if constexpr (M < NM) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    constexpr int nr = items_at(NR, NM, M);
+    constexpr int nr = reads_at(C::RS, C::FM, C::FN, M);
     constexpr int nl = items_at(NL, NM, M);
     if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);  // LDS reads
     if constexpr (nl > 0) __builtin_amdgcn_sched_group_barrier(0x010, nl, 0);  // loads
-    sched_pattern<NM, NR, NL, M + 1>();
+    sched_pattern<C, NL, M + 1>();
+  }
+}
+
+// Fragment read R of the next k-step (A fragments first, then B).
+template <class C, int R>
+__device__ __forceinline__ void read_one(Frags<C>& nxt, const char* rstage, int rks, int wm,
+                                         int wn, int lane) {
+  if constexpr (R < C::FM) {
+    nxt.a[R] = *reinterpret_cast<const half8*>(
+        rstage + frag_off<C>(wm * C::WM + R * C::M::DIM, rks, lane));
+  } else {
+    nxt.b[R - C::FM] = *reinterpret_cast<const half8*>(
+        rstage + C::A_BYTES + frag_off<C>(wn * C::WN + (R - C::FM) * C::M::DIM, rks, lane));
+  }
+}
+
+template <class C, int R, int END>
+__device__ __forceinline__ void read_range(Frags<C>& nxt, const char* rstage, int rks, int wm,
+                                           int wn, int lane) {
+  if constexpr (R < END) {
+    read_one<C, read_frag(C::RS, C::FM, C::FN, R)>(nxt, rstage, rks, wm, wn, lane);
+    read_range<C, R + 1, END>(nxt, rstage, rks, wm, wn, lane);
+  }
+}
+
+// MFMA M of one k-step on `cur`, followed by the fragment reads and the loads
+// assigned to it; recursion keeps every accumulator and fragment index a
+// compile-time constant, whatever the number of blocks.
+template <class C, int LFIRST, int NL, int M>
+__device__ __forceinline__ void kstep_from(typename C::acc_t (&acc)[C::FM][C::FN],
+                                           const Frags<C>& cur, Frags<C>& nxt, const char* rstage,
+                                           int rks, int wm, int wn, int lane, char* lstage,
+                                           const Operands& op, const LoadMap<C, C::A_LOADS>& ma,
+                                           const LoadMap<C, C::B_LOADS>& mb, int wave, int k0) {
+  constexpr int NM = C::FM * C::FN;
+  static_assert(read_slots_sorted(C::RS, C::FM, C::FN), "reads must be in slot order");
+  if constexpr (M < NM) {
+    constexpr int i = M / C::FN, j = M % C::FN;
+    acc[i][j] = C::M::mma(cur.b[j], cur.a[i], acc[i][j]);
+    constexpr int r0 = reads_before(C::RS, C::FM, C::FN, M);
+    read_range<C, r0, r0 + reads_at(C::RS, C::FM, C::FN, M)>(nxt, rstage, rks, wm, wn, lane);
+    if constexpr (NL > 0) {
+      constexpr int l0 = items_before(NL, NM, M);
+      constexpr int nl = items_at(NL, NM, M);
+#pragma unroll
+      for (int l = 0; l < nl; ++l) issue_one<C>(LFIRST + l0 + l, lstage, op, ma, mb, wave, k0);
+    }
+    kstep_from<C, LFIRST, NL, M + 1>(acc, cur, nxt, rstage, rks, wm, wn, lane, lstage, op, ma, mb,
+                                     wave, k0);
   }
 }
 
@@ -220,72 +371,77 @@ __device__ __forceinline__ void sched_pattern() {
 // loads assigned to it, so neither the LDS reads nor the load issue (which
 // can stall while the address FIFO is full) holds back a run of MFMAs.
 template <class C, int LFIRST, int NL>
-__device__ __forceinline__ void kstep(f32x16 (&acc)[C::FM][C::FN], const Frags<C>& cur,
+__device__ __forceinline__ void kstep(typename C::acc_t (&acc)[C::FM][C::FN], const Frags<C>& cur,
                                       Frags<C>& nxt, const char* rstage, int rks, int wm, int wn,
                                       int lane, char* lstage, const Operands& op,
                                       const LoadMap<C, C::A_LOADS>& ma,
                                       const LoadMap<C, C::B_LOADS>& mb, int wave, int k0) {
-  constexpr int NM = C::FM * C::FN;
-  constexpr int NR = C::FM + C::FN;
-#pragma unroll
-  for (int m = 0; m < NM; ++m) {
-    const int i = m / C::FN, j = m % C::FN;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0);
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      if (r * NM / NR == m) {
-        if (r < C::FM) {
-          const int row = wm * C::WM + r * 32 + (lane & 31);
-          nxt.a[r] = *reinterpret_cast<const half8*>(rstage + frag_off<C>(row, rks, lane));
-        } else {
-          const int row = wn * C::WN + (r - C::FM) * 32 + (lane & 31);
-          nxt.b[r - C::FM] =
-              *reinterpret_cast<const half8*>(rstage + C::A_BYTES + frag_off<C>(row, rks, lane));
-        }
-      }
-    }
-#pragma unroll
-    for (int l = 0; l < NL; ++l)
-      if (NL > 0 && l * NM / NL == m) issue_one<C>(LFIRST + l, lstage, op, ma, mb, wave, k0);
-  }
-  sched_pattern<NM, NR, NL, 0>();
+  kstep_from<C, LFIRST, NL, 0>(acc, cur, nxt, rstage, rks, wm, wn, lane, lstage, op, ma, mb, wave,
+                               k0);
+  sched_pattern<C, NL, 0>();
 }
 
 // The k-steps of one stage. K-steps 0..LK-1 also issue the loads of the stage
 // entering the ring (all in k-step 0 with a 2-deep ring, whose next stage must
 // land within this one). Before the last k-step the next stage is handed over
 // (its loads landed in every wave, all reads of the freed buffer done), and
-// that k-step reads the next stage's first fragments.
-template <class C, int KS>
-__device__ __forceinline__ void run_ksteps(f32x16 (&acc)[C::FM][C::FN], Frags<C> (&fr)[2],
+// that k-step reads the next stage's first fragments. Fragment buffers
+// alternate per k-step: k-step KS computes from fr[(KS + PH) & 1], PH being
+// the parity of the k-steps before this stage (always 0 when KSTEPS is even).
+template <class C, int KS, int PH>
+__device__ __forceinline__ void run_ksteps(typename C::acc_t (&acc)[C::FM][C::FN], Frags<C> (&fr)[2],
                                            const char* stage, const char* nstage, int wm, int wn,
                                            int lane, char* lstage, const Operands& op,
                                            const LoadMap<C, C::A_LOADS>& ma,
                                            const LoadMap<C, C::B_LOADS>& mb, int wave, int k0) {
-  static_assert(C::KSTEPS % 2 == 0, "fragment double buffer alternates per k-step");
-  constexpr int LK = C::STAGES == 2 ? 1 : C::KSTEPS - 1;
+  constexpr int LK = C::STAGES == 2 || C::KSTEPS == 1 ? 1 : C::KSTEPS - 1;
   constexpr int LF = KS < LK ? KS * C::LOADS / LK : 0;
   constexpr int NL = KS < LK ? (KS + 1) * C::LOADS / LK - LF : 0;
+  // At the hand-over barrier the stages after the next one may still be in
+  // flight: S - 2 of them when this stage's loads were issued before the
+  // barrier, one fewer when they go out with the last k-step (KSTEPS == 1).
+  constexpr bool kLoadsBefore = LK <= C::KSTEPS - 1;
+  constexpr int kPending = C::LOADS * (C::STAGES - 2 - (kLoadsBefore ? 0 : 1));
+  static_assert(kLoadsBefore || C::STAGES >= 3, "one k-step per stage needs 3 or more stages");
   if constexpr (KS < C::KSTEPS - 1) {
-    kstep<C, LF, NL>(acc, fr[KS & 1], fr[(KS + 1) & 1], stage, KS + 1, wm, wn, lane, lstage, op,
-                     ma, mb, wave, k0);
-    run_ksteps<C, KS + 1>(acc, fr, stage, nstage, wm, wn, lane, lstage, op, ma, mb, wave, k0);
+    kstep<C, LF, NL>(acc, fr[(KS + PH) & 1], fr[(KS + PH + 1) & 1], stage, KS + 1, wm, wn, lane,
+                     lstage, op, ma, mb, wave, k0);
+    run_ksteps<C, KS + 1, PH>(acc, fr, stage, nstage, wm, wn, lane, lstage, op, ma, mb, wave, k0);
   } else {
-    wait_vm<C::LOADS * (C::STAGES - 2)>();
+    wait_vm<kPending>();
     wait_lgkm_zero();
     lds_barrier();
-    kstep<C, LF, NL>(acc, fr[KS & 1], fr[(KS + 1) & 1], nstage, 0, wm, wn, lane, lstage, op, ma,
-                     mb, wave, k0);
+    kstep<C, LF, NL>(acc, fr[(KS + PH) & 1], fr[(KS + PH + 1) & 1], nstage, 0, wm, wn, lane, lstage,
+                     op, ma, mb, wave, k0);
   }
 }
 
+// One stage of the main loop: k-iteration `kit` (absolute, in BK units),
+// held in ring buffer st; loads k-iteration kit + STAGES - 1 into the buffer
+// freed at the last barrier and advances st.
+template <class C, int PH>
+__device__ __forceinline__ void run_stage(typename C::acc_t (&acc)[C::FM][C::FN],
+                                          Frags<C> (&fr)[2], char* smem, int& st, int kit, int wm,
+                                          int wn, int lane, const Operands& op,
+                                          const LoadMap<C, C::A_LOADS>& ma,
+                                          const LoadMap<C, C::B_LOADS>& mb, int wave) {
+  const int st_next = st + 1 == C::STAGES ? 0 : st + 1;
+  const int st_load = st == 0 ? C::STAGES - 1 : st - 1;
+  run_ksteps<C, 0, PH>(acc, fr, smem + st * C::STAGE_BYTES, smem + st_next * C::STAGE_BYTES, wm,
+                       wn, lane, smem + st_load * C::STAGE_BYTES, op, ma, mb, wave,
+                       (kit + C::STAGES - 1) * C::BK);
+  st = st_next;
+}
+
 // Partial tiles in the workspace are kept in the accumulators' own layout:
-// float4 number (((i * FN + j) * 4 + g) * WAVES + wave) * 64 + lane holds
-// registers 4g..4g+3 of block (i, j) of that wave and lane, so each store and
-// each load of a wave covers 1 KiB of consecutive bytes.
+// float4 number (((i * FN + j) * GROUPS + g) * WAVES + wave) * 64 + lane
+// holds registers 4g..4g+3 of block (i, j) of that wave and lane, so each
+// store and each load of a wave covers 1 KiB of consecutive bytes.
 template <class C>
-__device__ __forceinline__ void write_partial(f32x4* part, const f32x16 (&acc)[C::FM][C::FN],
+__device__ __forceinline__ void write_partial(f32x4* part,
+                                              const typename C::acc_t (&acc)[C::FM][C::FN],
                                               int wave, int lane) {
+  constexpr int G = C::M::GROUPS;
   // Buffer stores: the tile's base in the descriptor, one per-lane offset, and
   // each store's fixed offset in a scalar register (no per-store addresses).
   const __amdgpu_buffer_rsrc_t r =
@@ -296,11 +452,11 @@ __device__ __forceinline__ void write_partial(f32x4* part, const f32x16 (&acc)[C
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < G; ++g) {
         const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                          acc[i][j][4 * g + 3]};
         __builtin_amdgcn_raw_buffer_store_b128(
-            __builtin_bit_cast(u32x4, v), r, voff, ((i * C::FN + j) * 4 + g) * C::WAVES * 64 * 16,
+            __builtin_bit_cast(u32x4, v), r, voff, ((i * C::FN + j) * G + g) * C::WAVES * 64 * 16,
             0);
       }
 }
@@ -339,11 +495,11 @@ __device__ __forceinline__ void reduce_range(const GemmParams& p, const f32x4* p
       const int lane = e % 64;
       const int wave = (e / 64) % C::WAVES;
       const int rest = e / (64 * C::WAVES);
-      const int g = rest % 4;
-      const int i = (rest / 4) / C::FN;
-      const int j = (rest / 4) % C::FN;
-      const int m = m0 + (wave / C::WGN) * C::WM + i * 32 + (lane & 31);
-      const int n = n0 + (wave % C::WGN) * C::WN + j * 32 + 8 * g + 4 * (lane >> 5);
+      const int g = rest % C::M::GROUPS;
+      const int i = (rest / C::M::GROUPS) / C::FN;
+      const int j = (rest / C::M::GROUPS) % C::FN;
+      const int m = m0 + (wave / C::WGN) * C::WM + i * C::M::DIM + C::M::acc_m(lane);
+      const int n = n0 + (wave % C::WGN) * C::WN + j * C::M::DIM + C::M::acc_n(g, lane);
       if (m >= p.M) continue;
       float* crow = p.C + (int64_t)m * p.ldc;
       if (n + 3 < p.N && p.c_vec4) {
@@ -358,22 +514,22 @@ __device__ __forceinline__ void reduce_range(const GemmParams& p, const f32x4* p
 }
 
 // Write the wave's accumulators to C (a tile computed by one unit alone).
-// Lane l holds, for block (i, j) and register v = 4g + q:
-//   row    m = m_base + 32 i + l % 32
-//   column n = n_base + 32 j + 8 g + 4 (l / 32) + q
+// Lane l holds, for block (i, j) and register v = 4g + q, row
+// m_base + DIM i + acc_m(l) and column n_base + DIM j + acc_n(g, l) + q.
 template <class C>
-__device__ __forceinline__ void epilogue(const GemmParams& p, const f32x16 (&acc)[C::FM][C::FN],
+__device__ __forceinline__ void epilogue(const GemmParams& p,
+                                         const typename C::acc_t (&acc)[C::FM][C::FN],
                                          int m_base, int n_base, int lane) {
   const bool full = m_base + C::WM <= p.M && n_base + C::WN <= p.N;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
-    const int m = m_base + i * 32 + (lane & 31);
+    const int m = m_base + i * C::M::DIM + C::M::acc_m(lane);
     float* crow = p.C + (int64_t)m * p.ldc;
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n_base + j * 32 + 8 * g + 4 * (lane >> 5);
+      for (int g = 0; g < C::M::GROUPS; ++g) {
+        const int n = n_base + j * C::M::DIM + C::M::acc_n(g, lane);
         const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                          acc[i][j][4 * g + 3]};
         if (full && p.c_vec4) {
@@ -421,11 +577,11 @@ void gemm_tiled_kernel(GemmParams p) {
     make_load_map<C, C::A_LOADS>(ma, wave, lane, p.M - m0, p.lda, k_limit);
     make_load_map<C, C::B_LOADS>(mb, wave, lane, p.N - n0, p.ldb, k_limit);
 
-    f32x16 acc[C::FM][C::FN];
+    typename C::acc_t acc[C::FM][C::FN];
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
+      for (int j = 0; j < C::FN; ++j) acc[i][j] = typename C::acc_t{};
 
     // The previous unit's loads have landed and every wave has finished
     // reading LDS, so the ring buffers can be refilled.
@@ -446,15 +602,19 @@ void gemm_tiled_kernel(GemmParams p) {
     read_frags<C>(smem, 0, wm, wn, lane, fr[0]);
 
     int st = 0;  // ring buffer holding stage `it`
-    for (int it = 0; it < nk; ++it) {
-      const int st_next = st + 1 == C::STAGES ? 0 : st + 1;
-      const int st_load = st == 0 ? C::STAGES - 1 : st - 1;  // freed at the last barrier
-      const char* stage = smem + st * C::STAGE_BYTES;
-      char* lstage = smem + st_load * C::STAGE_BYTES;
-      const int k0_load = (seg.k_begin + it + C::STAGES - 1) * C::BK;
-      run_ksteps<C, 0>(acc, fr, stage, smem + st_next * C::STAGE_BYTES, wm, wn, lane, lstage, op,
-                       ma, mb, wave, k0_load);
-      st = st_next;
+    if constexpr (C::KSTEPS % 2 == 0) {
+      for (int it = 0; it < nk; ++it)
+        run_stage<C, 0>(acc, fr, smem, st, seg.k_begin + it, wm, wn, lane, op, ma, mb, wave);
+    } else {
+      // One k-step per stage: the fragment buffers swap roles every stage,
+      // so stages go in pairs and each copy of the body has fixed roles.
+      int it = 0;
+      for (; it + 1 < nk; it += 2) {
+        run_stage<C, 0>(acc, fr, smem, st, seg.k_begin + it, wm, wn, lane, op, ma, mb, wave);
+        run_stage<C, 1>(acc, fr, smem, st, seg.k_begin + it + 1, wm, wn, lane, op, ma, mb, wave);
+      }
+      if (it < nk)
+        run_stage<C, 0>(acc, fr, smem, st, seg.k_begin + it, wm, wn, lane, op, ma, mb, wave);
     }
 
     if (seg.role == ROLE_ONLY) {
@@ -535,28 +695,32 @@ __global__ __launch_bounds__(256) void gemm_general_kernel(GemmParams p, int32_t
   }
 }
 
-using C0 = Cfg<256, 256, 64, 2, 2, 2>;
-using C1 = Cfg<256, 256, 32, 4, 2, 2>;
-using C2 = Cfg<256, 256, 64, 2, 2, 4>;
-using C3 = Cfg<256, 128, 64, 3, 2, 2>;
-using C4 = Cfg<128, 128, 64, 4, 2, 2>;
-using C5 = Cfg<128, 64, 64, 4, 2, 2>;
-using C6 = Cfg<64, 64, 64, 4, 2, 2>;
-using C7 = Cfg<256, 256, 32, 5, 2, 2>;
-using C8 = Cfg<256, 256, 32, 4, 2, 4>;
-using C9 = Cfg<256, 256, 32, 5, 2, 4>;
+#define G16_CFG(id, name, bm, bn, bk, st, wgm, wgn, mi, rs) \
+  using K##id = Cfg<bm, bn, bk, st, wgm, wgn, mi, rs>;
+G16_TILED_KERNELS(G16_CFG)
+#undef G16_CFG
 
 template <class C>
 constexpr KernelInfo info_of(const char* name) {
-  return KernelInfo{C::BM, C::BN, C::BK, C::STAGES, C::WAVES, C::LDS_BYTES, name};
+  return KernelInfo{C::BM, C::BN, C::BK, C::STAGES, C::WAVES, C::LDS_BYTES, C::MI, name};
 }
 
+// Names: BMxBNxBK, ring depth, waves, "_m16" for the 16x16x32 MFMA and "_rs"
+// for late fragment reads.
 constexpr KernelInfo kInfos[KID_COUNT] = {
-    info_of<C0>("256x256x64_s2_w4"), info_of<C1>("256x256x32_s4_w4"),
-    info_of<C2>("256x256x64_s2_w8"), info_of<C3>("256x128x64_s3_w4"),
-    info_of<C4>("128x128x64_s4_w4"), info_of<C5>("128x64x64_s4_w4"),
-    info_of<C6>("64x64x64_s4_w4"), info_of<C7>("256x256x32_s5_w4"),
-    info_of<C8>("256x256x32_s4_w8"), info_of<C9>("256x256x32_s5_w8"),
+    info_of<K0>("256x256x64_s2_w4"),      info_of<K1>("256x256x32_s4_w4"),
+    info_of<K2>("256x256x64_s2_w8"),      info_of<K3>("256x128x64_s3_w4"),
+    info_of<K4>("128x128x64_s4_w4"),      info_of<K5>("128x64x64_s4_w4"),
+    info_of<K6>("64x64x64_s4_w4"),        info_of<K7>("256x256x32_s5_w4"),
+    info_of<K8>("256x256x32_s4_w8"),      info_of<K9>("256x256x32_s5_w8"),
+    info_of<K10>("256x256x64_s2_w4_m16"), info_of<K11>("256x256x32_s4_w4_m16"),
+    info_of<K12>("256x256x32_s5_w4_m16"), info_of<K13>("256x256x64_s2_w8_m16"),
+    info_of<K14>("256x256x32_s5_w8_m16"), info_of<K15>("256x128x64_s3_w4_m16"),
+    info_of<K16>("128x128x64_s4_w4_m16"), info_of<K17>("128x64x64_s4_w4_m16"),
+    info_of<K18>("64x64x64_s4_w4_m16"),   info_of<K19>("256x256x32_s3_w4_m16"),
+    info_of<K20>("256x256x32_s5_w8_m16_rs"), info_of<K21>("256x256x64_s2_w8_m16_rs"),
+    info_of<K22>("256x256x32_s4_w8_m16_rs"), info_of<K23>("256x256x32_s5_w4_m16_rs"),
+    info_of<K24>("256x256x64_s2_w4_m16_rs"),
 };
 
 template <class C>
@@ -591,35 +755,23 @@ const KernelInfo* kernel_info(int32_t kid) {
 }
 
 hipError_t launch_tiled(int32_t kid, const GemmParams& p, hipStream_t stream) {
+#define G16_LAUNCH(id, name, ...) \
+  case name: return launch_cfg<K##id>(p, stream);
   switch (kid) {
-    case KID_256x256x64_S2_W4: return launch_cfg<C0>(p, stream);
-    case KID_256x256x32_S4_W4: return launch_cfg<C1>(p, stream);
-    case KID_256x256x64_S2_W8: return launch_cfg<C2>(p, stream);
-    case KID_256x128x64_S3_W4: return launch_cfg<C3>(p, stream);
-    case KID_128x128x64_S4_W4: return launch_cfg<C4>(p, stream);
-    case KID_128x64x64_S4_W4: return launch_cfg<C5>(p, stream);
-    case KID_64x64x64_S4_W4: return launch_cfg<C6>(p, stream);
-    case KID_256x256x32_S5_W4: return launch_cfg<C7>(p, stream);
-    case KID_256x256x32_S4_W8: return launch_cfg<C8>(p, stream);
-    case KID_256x256x32_S5_W8: return launch_cfg<C9>(p, stream);
+    G16_TILED_KERNELS(G16_LAUNCH)
     default: return hipErrorInvalidValue;
   }
+#undef G16_LAUNCH
 }
 
 int32_t tiled_occupancy(int32_t kid) {
+#define G16_OCC(id, name, ...) \
+  case name: return occupancy_cfg<K##id>();
   switch (kid) {
-    case KID_256x256x64_S2_W4: return occupancy_cfg<C0>();
-    case KID_256x256x32_S4_W4: return occupancy_cfg<C1>();
-    case KID_256x256x64_S2_W8: return occupancy_cfg<C2>();
-    case KID_256x128x64_S3_W4: return occupancy_cfg<C3>();
-    case KID_128x128x64_S4_W4: return occupancy_cfg<C4>();
-    case KID_128x64x64_S4_W4: return occupancy_cfg<C5>();
-    case KID_64x64x64_S4_W4: return occupancy_cfg<C6>();
-    case KID_256x256x32_S5_W4: return occupancy_cfg<C7>();
-    case KID_256x256x32_S4_W8: return occupancy_cfg<C8>();
-    case KID_256x256x32_S5_W8: return occupancy_cfg<C9>();
+    G16_TILED_KERNELS(G16_OCC)
     default: return 0;
   }
+#undef G16_OCC
 }
 
 hipError_t launch_general(const GemmParams& p, hipStream_t stream) {

@@ -247,11 +247,16 @@ def test_subnormal_inputs():
 
 # --- every kernel variant and schedule mode ---------------------------------
 
-PLANS = [f"kid={k}" for k in range(10)] + [
+# Tiled kernel ids 0-9 use v_mfma_f32_32x32x16_f16, 10-24 v_mfma_f32_16x16x32_f16.
+PLANS = [f"kid={k}" for k in range(25)] + [
     "kid=0,mode=1,splits=3", "kid=0,mode=2", "kid=0,mode=2,grid=37",
     "kid=4,mode=2,grid=100", "kid=6,mode=1,splits=5", "kid=2,mode=2,grid=64",
     "kid=1,mode=1,splits=2", "kid=3,mode=2,grid=29", "kid=5,mode=2,grid=130",
     "kid=7,mode=1,splits=4", "kid=9,mode=2", "kid=4,mode=1,splits=3,grid=40",
+    "kid=10,mode=1,splits=3", "kid=12,mode=2,grid=37", "kid=15,mode=2,grid=29",
+    "kid=11,mode=1,splits=2", "kid=19,mode=2", "kid=16,mode=1,splits=3,grid=40",
+    "kid=14,mode=2,grid=64", "kid=18,mode=1,splits=5", "kid=20,mode=1,splits=3",
+    "kid=21,mode=2,grid=37", "kid=22,mode=2", "kid=24,mode=1,splits=2",
 ]
 
 
@@ -268,6 +273,21 @@ def test_forced_plans(plan, monkeypatch):
     B = inputs.uniform(N, K, 134)
     ref, S = oracle.gemm_abt(A, B)
     assert_tol(run(A, B), ref, S, f"{plan} uniform")
+
+
+@pytest.mark.parametrize("kid", [0, 7, 10, 11, 12, 19, 20, 22, 23])
+@pytest.mark.parametrize("K", [24, 72, 200])
+def test_forced_plans_short_k(kid, K, monkeypatch):
+    """K of one to a few k-tiles, odd and even counts (one k-step per stage
+    runs its stages in pairs plus a tail)."""
+    monkeypatch.setenv("GEMM_F16_PLAN", f"kid={kid}")
+    M, N = 300, 264
+    Ai, Bi = inputs.integer(M, K, 151), inputs.integer(N, K, 152)
+    ref, _ = oracle.gemm_abt(Ai, Bi)
+    assert_exact(run(Ai, Bi), ref, f"kid={kid} K={K} integer")
+    A, B = inputs.uniform(M, K, 153), inputs.uniform(N, K, 154)
+    ref, S = oracle.gemm_abt(A, B)
+    assert_tol(run(A, B), ref, S, f"kid={kid} K={K} uniform")
 
 
 # --- invariants -------------------------------------------------------------
