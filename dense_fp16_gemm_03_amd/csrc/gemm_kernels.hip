@@ -409,7 +409,12 @@ __device__ __forceinline__ void run_ksteps(typename C::acc_t (&acc)[C::FM][C::FN
     run_ksteps<C, KS + 1, PH>(acc, fr, stage, nstage, wm, wn, lane, lstage, op, ma, mb, wave, k0);
   } else {
     wait_vm<kPending>();
-    wait_lgkm_zero();
+    // With several k-steps a stage, this barrier also frees the current
+    // buffer (refilled from the next stage's first k-step), so every read of
+    // it must have returned. With one, the buffer refilled after it was last
+    // read before the previous barrier, and the fragments in flight are only
+    // waited for where the MFMAs use them.
+    if constexpr (C::KSTEPS > 1) wait_lgkm_zero();
     lds_barrier();
     kstep<C, LF, NL>(acc, fr[(KS + PH) & 1], fr[(KS + PH + 1) & 1], nstage, 0, wm, wn, lane, lstage,
                      op, ma, mb, wave, k0);
