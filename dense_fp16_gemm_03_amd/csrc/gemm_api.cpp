@@ -19,11 +19,9 @@ namespace {
 using namespace g16;
 
 constexpr int32_t kDefaultCUs = 256;  // MI355X: 8 XCDs x 32 CUs
-// Kernel for large squares (one 256x256 tile or more per CU): 16x16x32 MFMA,
-// two waves per SIMD, fragment reads placed after their last use.
-constexpr int32_t KID_LARGE = KID_256x256x32_S5_W8_M16_RS;
-// Kernel for long-K shapes with fewer 256x256 tiles than CUs.
-constexpr int32_t KID_LONG_K = KID_256x128x64_S3_W4_M16;
+// Kernel for large squares and for long K: 256x256 tiles, 16x16x32 MFMA,
+// two waves per SIMD in the ping-pong main loop.
+constexpr int32_t KID_LARGE = KID_256x256x32_S5_W8_M16_PP;
 
 struct Plan {
   int32_t kid = -1;       // tiled kernel id, KID_GENERAL, or -1 (nothing to do)
@@ -109,8 +107,8 @@ bool tiled_eligible(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
 // set from measurements on the MI355X:
 //   * at least one 256x256 tile per CU: 256x256 tiles, data-parallel,
 //     persistent grid walking the tiles by stride;
-//   * fewer tiles but long K (>= 64 k-steps of 64): 256x128 tiles with K
-//     split so tiles x splits fills the CUs (each share keeps >= 8 k-steps);
+//   * fewer tiles but long K (>= 128 k-steps of 32): the same tiles with K
+//     split so tiles x splits fills the CUs (each share keeps >= 64 k-steps);
 //   * small problems: 128x128 tiles (64x64 when there are fewer than 16 of
 //     them), data-parallel; the splits' reduce pass costs more than it gains.
 Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
@@ -125,14 +123,13 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
   int32_t splits = 1;
   {
     const int64_t t256 = cdiv(M, 256) * cdiv(N, 256);
-    const int64_t k64 = cdiv(K, 64);
+    const int64_t k32 = cdiv(K, 32);
     if (t256 >= cus) {
       kid = KID_LARGE;
-    } else if (k64 >= 64) {
-      kid = KID_LONG_K;
-      const int64_t tiles = cdiv(M, 256) * cdiv(N, 128);
-      int64_t sp = tiles >= cus ? 1 : cus / tiles;
-      if (sp > k64 / 8) sp = k64 / 8;
+    } else if (k32 >= 128) {
+      kid = KID_LARGE;
+      int64_t sp = cus / t256;
+      if (sp > k32 / 64) sp = k32 / 64;  // each share keeps >= 64 k-steps of 32
       splits = (int32_t)std::max<int64_t>(sp, 1);
       mode = splits > 1 ? MODE_SPLIT : MODE_DATA_PARALLEL;
     } else {

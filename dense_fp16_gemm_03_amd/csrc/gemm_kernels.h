@@ -13,39 +13,46 @@ namespace g16 {
 // Tiled MFMA kernel variants: macro tile BM x BN, k-tile BK, ring depth
 // STAGES, a WGM x WGN grid of waves (each wave owns BM/WGM x BN/WGN) and the
 // MFMA shape (32: v_mfma_f32_32x32x16_f16, 16: v_mfma_f32_16x16x32_f16).
-// X(id, enum name, BM, BN, BK, STAGES, WGM, WGN, MFMA, RS); RS 1 issues each
-// next-k-step fragment read right after the last use of the one it replaces.
+// X(id, enum name, BM, BN, BK, STAGES, WGM, WGN, MFMA, RS, PP); RS 1 issues
+// each next-k-step fragment read right after the last use of the one it
+// replaces; PP 1 selects the ping-pong main loop (two wave groups, one
+// computing while the other reads LDS and issues loads).
 #define G16_TILED_KERNELS(X)                                       \
-  X(0, KID_256x256x64_S2_W4, 256, 256, 64, 2, 2, 2, 32, 0)            \
-  X(1, KID_256x256x32_S4_W4, 256, 256, 32, 4, 2, 2, 32, 0)            \
-  X(2, KID_256x256x64_S2_W8, 256, 256, 64, 2, 2, 4, 32, 0)            \
-  X(3, KID_256x128x64_S3_W4, 256, 128, 64, 3, 2, 2, 32, 0)            \
-  X(4, KID_128x128x64_S4_W4, 128, 128, 64, 4, 2, 2, 32, 0)            \
-  X(5, KID_128x64x64_S4_W4, 128, 64, 64, 4, 2, 2, 32, 0)              \
-  X(6, KID_64x64x64_S4_W4, 64, 64, 64, 4, 2, 2, 32, 0)                \
-  X(7, KID_256x256x32_S5_W4, 256, 256, 32, 5, 2, 2, 32, 0)            \
-  X(8, KID_256x256x32_S4_W8, 256, 256, 32, 4, 2, 4, 32, 0)            \
-  X(9, KID_256x256x32_S5_W8, 256, 256, 32, 5, 2, 4, 32, 0)            \
-  X(10, KID_256x256x64_S2_W4_M16, 256, 256, 64, 2, 2, 2, 16, 0)       \
-  X(11, KID_256x256x32_S4_W4_M16, 256, 256, 32, 4, 2, 2, 16, 0)       \
-  X(12, KID_256x256x32_S5_W4_M16, 256, 256, 32, 5, 2, 2, 16, 0)       \
-  X(13, KID_256x256x64_S2_W8_M16, 256, 256, 64, 2, 2, 4, 16, 0)       \
-  X(14, KID_256x256x32_S5_W8_M16, 256, 256, 32, 5, 2, 4, 16, 0)       \
-  X(15, KID_256x128x64_S3_W4_M16, 256, 128, 64, 3, 2, 2, 16, 0)       \
-  X(16, KID_128x128x64_S4_W4_M16, 128, 128, 64, 4, 2, 2, 16, 0)       \
-  X(17, KID_128x64x64_S4_W4_M16, 128, 64, 64, 4, 2, 2, 16, 0)         \
-  X(18, KID_64x64x64_S4_W4_M16, 64, 64, 64, 4, 2, 2, 16, 0)           \
-  X(19, KID_256x256x32_S3_W4_M16, 256, 256, 32, 3, 2, 2, 16, 0)   \
-  X(20, KID_256x256x32_S5_W8_M16_RS, 256, 256, 32, 5, 2, 4, 16, 1) \
-  X(21, KID_256x256x64_S2_W8_M16_RS, 256, 256, 64, 2, 2, 4, 16, 1) \
-  X(22, KID_256x256x32_S4_W8_M16_RS, 256, 256, 32, 4, 2, 4, 16, 1) \
-  X(23, KID_256x256x32_S5_W4_M16_RS, 256, 256, 32, 5, 2, 2, 16, 1) \
-  X(24, KID_256x256x64_S2_W4_M16_RS, 256, 256, 64, 2, 2, 2, 16, 1)
+  X(0, KID_256x256x64_S2_W4, 256, 256, 64, 2, 2, 2, 32, 0, 0)            \
+  X(1, KID_256x256x32_S4_W4, 256, 256, 32, 4, 2, 2, 32, 0, 0)            \
+  X(2, KID_256x256x64_S2_W8, 256, 256, 64, 2, 2, 4, 32, 0, 0)            \
+  X(3, KID_256x128x64_S3_W4, 256, 128, 64, 3, 2, 2, 32, 0, 0)            \
+  X(4, KID_128x128x64_S4_W4, 128, 128, 64, 4, 2, 2, 32, 0, 0)            \
+  X(5, KID_128x64x64_S4_W4, 128, 64, 64, 4, 2, 2, 32, 0, 0)              \
+  X(6, KID_64x64x64_S4_W4, 64, 64, 64, 4, 2, 2, 32, 0, 0)                \
+  X(7, KID_256x256x32_S5_W4, 256, 256, 32, 5, 2, 2, 32, 0, 0)            \
+  X(8, KID_256x256x32_S4_W8, 256, 256, 32, 4, 2, 4, 32, 0, 0)            \
+  X(9, KID_256x256x32_S5_W8, 256, 256, 32, 5, 2, 4, 32, 0, 0)            \
+  X(10, KID_256x256x64_S2_W4_M16, 256, 256, 64, 2, 2, 2, 16, 0, 0)       \
+  X(11, KID_256x256x32_S4_W4_M16, 256, 256, 32, 4, 2, 2, 16, 0, 0)       \
+  X(12, KID_256x256x32_S5_W4_M16, 256, 256, 32, 5, 2, 2, 16, 0, 0)       \
+  X(13, KID_256x256x64_S2_W8_M16, 256, 256, 64, 2, 2, 4, 16, 0, 0)       \
+  X(14, KID_256x256x32_S5_W8_M16, 256, 256, 32, 5, 2, 4, 16, 0, 0)       \
+  X(15, KID_256x128x64_S3_W4_M16, 256, 128, 64, 3, 2, 2, 16, 0, 0)       \
+  X(16, KID_128x128x64_S4_W4_M16, 128, 128, 64, 4, 2, 2, 16, 0, 0)       \
+  X(17, KID_128x64x64_S4_W4_M16, 128, 64, 64, 4, 2, 2, 16, 0, 0)         \
+  X(18, KID_64x64x64_S4_W4_M16, 64, 64, 64, 4, 2, 2, 16, 0, 0)           \
+  X(19, KID_256x256x32_S3_W4_M16, 256, 256, 32, 3, 2, 2, 16, 0, 0)   \
+  X(20, KID_256x256x32_S5_W8_M16_RS, 256, 256, 32, 5, 2, 4, 16, 1, 0) \
+  X(21, KID_256x256x64_S2_W8_M16_RS, 256, 256, 64, 2, 2, 4, 16, 1, 0) \
+  X(22, KID_256x256x32_S4_W8_M16_RS, 256, 256, 32, 4, 2, 4, 16, 1, 0) \
+  X(23, KID_256x256x32_S5_W4_M16_RS, 256, 256, 32, 5, 2, 2, 16, 1, 0) \
+  X(24, KID_256x256x64_S2_W4_M16_RS, 256, 256, 64, 2, 2, 2, 16, 1, 0) \
+  X(25, KID_256x256x32_S5_W8_M16_PP, 256, 256, 32, 5, 2, 4, 16, 0, 1) \
+  X(26, KID_256x256x32_S4_W8_M16_PP, 256, 256, 32, 4, 2, 4, 16, 0, 1) \
+  X(27, KID_256x256x32_S3_W8_M16_PP, 256, 256, 32, 3, 2, 4, 16, 0, 1) \
+  X(28, KID_256x256x32_S5_W8_PP, 256, 256, 32, 5, 2, 4, 32, 0, 1)     \
+  X(29, KID_256x128x32_S5_W8_M16_PP, 256, 128, 32, 5, 2, 4, 16, 0, 1)
 
 #define G16_KID_ENUM(id, name, ...) name = id,
 enum KernelId : int32_t {
   G16_TILED_KERNELS(G16_KID_ENUM)
-  KID_COUNT = 25,
+  KID_COUNT = 30,
   KID_GENERAL = 100  // any shape and alignment, 64 x 64 tiles, no LDS
 };
 #undef G16_KID_ENUM

@@ -97,12 +97,15 @@ struct Mma<16> {
 // evenly over the k-step's MFMAs; 1: each right after the last MFMA that uses
 // the fragment it replaces, so the current and next fragments barely overlap
 // in registers (for register-bound variants).
-template <int BM_, int BN_, int BK_, int STAGES_, int WGM_, int WGN_, int MI_ = 32, int RS_ = 0>
+// PP_: 1 selects the ping-pong main loop (gemm_pingpong_kernel, 8 waves).
+template <int BM_, int BN_, int BK_, int STAGES_, int WGM_, int WGN_, int MI_ = 32, int RS_ = 0,
+          int PP_ = 0>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
   static constexpr int WGM = WGM_, WGN = WGN_;
   static constexpr int MI = MI_;
   static constexpr int RS = RS_;
+  static constexpr int PP = PP_;
   using M = Mma<MI>;
   using acc_t = typename M::acc_t;
   static constexpr int WAVES = WGM * WGN;
@@ -176,6 +179,33 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// seg_at computes the same segment in every lane (its inputs are the
+// schedule and the workgroup index); this says so to the compiler, which
+// otherwise may keep the segment in vector registers and wrap each buffer
+// store that depends on it in a per-lane loop.
+__device__ __forceinline__ bool seg_at_uniform(const Sched& s, int32_t v, int32_t n, Segment* out) {
+  Segment t;
+  if (!seg_at(s, v, n, &t)) return false;
+  out->tile = __builtin_amdgcn_readfirstlane(t.tile);
+  out->tm = __builtin_amdgcn_readfirstlane(t.tm);
+  out->tn = __builtin_amdgcn_readfirstlane(t.tn);
+  out->k_begin = __builtin_amdgcn_readfirstlane(t.k_begin);
+  out->k_end = __builtin_amdgcn_readfirstlane(t.k_end);
+  out->role = __builtin_amdgcn_readfirstlane(t.role);
+  out->contributors = __builtin_amdgcn_readfirstlane(t.contributors);
+  out->index = __builtin_amdgcn_readfirstlane(t.index);
+  return true;
+}
+
+// A workgroup barrier that nothing is scheduled across, not even
+// instructions without memory operands (the ping-pong phases depend on
+// which MFMAs sit between which barriers).
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <class C>
@@ -563,7 +593,7 @@ void gemm_tiled_kernel(GemmParams p) {
   const int v = virtual_wg(blockIdx.x, p.s.grid, p.s.xcd_remap);
 
   Segment seg;
-  for (int n = 0; seg_at(p.s, v, n, &seg); ++n) {
+  for (int n = 0; seg_at_uniform(p.s, v, n, &seg); ++n) {
     const int m0 = seg.tm * C::BM;
     const int n0 = seg.tn * C::BN;
     const int nk = seg.k_end - seg.k_begin;
@@ -630,6 +660,116 @@ void gemm_tiled_kernel(GemmParams p) {
       write_partial<C>(p.partials + ((int64_t)seg.tile * p.s.slots + seg.index) * (C::BM * C::BN / 4),
                        acc, wave, lane);
     }
+  }
+}
+
+// Ping-pong main loop (8 waves, two per SIMD). The waves form two groups,
+// one wave of each on every SIMD (group 0: waves 0-3, group 1: waves 4-7),
+// and group 1 runs one phase behind group 0. A stage takes two phases per
+// wave, separated by workgroup barriers:
+//   memory phase:  read all of the stage's fragments from LDS, issue this
+//                  wave's loads of stage it + STAGES - 1, wait until stage
+//                  it + 1 has landed and the fragments have arrived;
+//   compute phase: the stage's MFMAs, from registers only.
+// So while one group computes, the other does its memory work and is
+// already waiting at the barrier when the computing group arrives: the MFMA
+// pipe of every SIMD is fed by one wave or the other through each barrier
+// (the ping-pong schedule the CUTLASS Hopper post describes for two consumer
+// warp groups, here across the waves sharing a SIMD).
+// Buffer reuse: stage j's buffer is refilled in memory phases j + 1 (group 0
+// after its compute phase j, which follows group 1's read of stage j across
+// a barrier) and later; stage j + 1 is complete in LDS before either group
+// reads it, since every wave waits for its share of it before the barrier
+// that opens group 0's memory phase j + 1.
+template <class C>
+__global__ __launch_bounds__(C::THREADS)
+__attribute__((amdgpu_waves_per_eu(C::WAVES_PER_EU, C::WAVES_PER_EU)))
+void gemm_pingpong_kernel(GemmParams p) {
+  static_assert(C::WAVES == 8, "ping-pong pairs two waves per SIMD");
+  static_assert(C::STAGES >= 3, "a stage is awaited while the next two are in flight");
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool late = wave >= 4;  // group 1
+  const int wm = wave / C::WGN;
+  const int wn = wave % C::WGN;
+  const int v = virtual_wg(blockIdx.x, p.s.grid, p.s.xcd_remap);
+
+  Segment seg;
+  for (int n = 0; seg_at_uniform(p.s, v, n, &seg); ++n) {
+    const int m0 = seg.tm * C::BM;
+    const int n0 = seg.tn * C::BN;
+    const int nk = seg.k_end - seg.k_begin;
+    const int k_limit = min_of(p.K, seg.k_end * C::BK);
+
+    Operands op;
+    op.ra = __builtin_amdgcn_make_buffer_rsrc((void*)(p.A + (int64_t)m0 * p.lda), (short)0,
+                                              kNumRecords, kBufferWord3);
+    op.rb = __builtin_amdgcn_make_buffer_rsrc((void*)(p.B + (int64_t)n0 * p.ldb), (short)0,
+                                              kNumRecords, kBufferWord3);
+    LoadMap<C, C::A_LOADS> ma;
+    LoadMap<C, C::B_LOADS> mb;
+    make_load_map<C, C::A_LOADS>(ma, wave, lane, p.M - m0, p.lda, k_limit);
+    make_load_map<C, C::B_LOADS>(mb, wave, lane, p.N - n0, p.ldb, k_limit);
+
+    typename C::acc_t acc[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) acc[i][j] = typename C::acc_t{};
+
+    // The previous unit's loads have landed and all LDS reads are done.
+    wait_vm<0>();
+    wait_lgkm_zero();
+    lds_barrier();
+#pragma unroll
+    for (int s = 0; s < C::STAGES - 1; ++s) {
+#pragma unroll
+      for (int j = 0; j < C::LOADS; ++j)
+        issue_one<C>(j, smem + s * C::STAGE_BYTES, op, ma, mb, wave, (seg.k_begin + s) * C::BK);
+    }
+    wait_vm<C::LOADS * (C::STAGES - 2)>();
+    phase_barrier();
+    if (late) phase_barrier();  // group 1 starts one phase behind
+
+    Frags<C> fr[C::KSTEPS];
+    int st = 0;
+    for (int it = 0; it < nk; ++it) {
+      const int st_load = st == 0 ? C::STAGES - 1 : st - 1;
+      const char* stage = smem + st * C::STAGE_BYTES;
+      // Memory phase.
+#pragma unroll
+      for (int ks = 0; ks < C::KSTEPS; ++ks) read_frags<C>(stage, ks, wm, wn, lane, fr[ks]);
+      const int k0 = (seg.k_begin + it + C::STAGES - 1) * C::BK;
+#pragma unroll
+      for (int j = 0; j < C::LOADS; ++j)
+        issue_one<C>(j, smem + st_load * C::STAGE_BYTES, op, ma, mb, wave, k0);
+      wait_vm<C::LOADS * (C::STAGES - 2)>();
+      wait_lgkm_zero();
+      phase_barrier();
+      // Compute phase.
+#pragma unroll
+      for (int ks = 0; ks < C::KSTEPS; ++ks)
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+            acc[i][j] = C::M::mma(fr[ks].b[j], fr[ks].a[i], acc[i][j]);
+      phase_barrier();
+      st = st + 1 == C::STAGES ? 0 : st + 1;
+    }
+
+    // Group 0 finishes while group 1 runs its last compute phase, then
+    // passes the barrier that matches group 1's extra one.
+    if (seg.role == ROLE_ONLY) {
+      epilogue<C>(p, acc, m0 + wm * C::WM, n0 + wn * C::WN, lane);
+    } else {
+      write_partial<C>(p.partials + ((int64_t)seg.tile * p.s.slots + seg.index) * (C::BM * C::BN / 4),
+                       acc, wave, lane);
+    }
+    if (!late) phase_barrier();
   }
 }
 
@@ -700,8 +840,8 @@ __global__ __launch_bounds__(256) void gemm_general_kernel(GemmParams p, int32_t
   }
 }
 
-#define G16_CFG(id, name, bm, bn, bk, st, wgm, wgn, mi, rs) \
-  using K##id = Cfg<bm, bn, bk, st, wgm, wgn, mi, rs>;
+#define G16_CFG(id, name, bm, bn, bk, st, wgm, wgn, mi, rs, pp) \
+  using K##id = Cfg<bm, bn, bk, st, wgm, wgn, mi, rs, pp>;
 G16_TILED_KERNELS(G16_CFG)
 #undef G16_CFG
 
@@ -710,8 +850,8 @@ constexpr KernelInfo info_of(const char* name) {
   return KernelInfo{C::BM, C::BN, C::BK, C::STAGES, C::WAVES, C::LDS_BYTES, C::MI, name};
 }
 
-// Names: BMxBNxBK, ring depth, waves, "_m16" for the 16x16x32 MFMA and "_rs"
-// for late fragment reads.
+// Names: BMxBNxBK, ring depth, waves, "_m16" for the 16x16x32 MFMA, "_rs"
+// for late fragment reads and "_pp" for the ping-pong main loop.
 constexpr KernelInfo kInfos[KID_COUNT] = {
     info_of<K0>("256x256x64_s2_w4"),      info_of<K1>("256x256x32_s4_w4"),
     info_of<K2>("256x256x64_s2_w8"),      info_of<K3>("256x128x64_s3_w4"),
@@ -726,11 +866,17 @@ constexpr KernelInfo kInfos[KID_COUNT] = {
     info_of<K20>("256x256x32_s5_w8_m16_rs"), info_of<K21>("256x256x64_s2_w8_m16_rs"),
     info_of<K22>("256x256x32_s4_w8_m16_rs"), info_of<K23>("256x256x32_s5_w4_m16_rs"),
     info_of<K24>("256x256x64_s2_w4_m16_rs"),
+    info_of<K25>("256x256x32_s5_w8_m16_pp"), info_of<K26>("256x256x32_s4_w8_m16_pp"),
+    info_of<K27>("256x256x32_s3_w8_m16_pp"), info_of<K28>("256x256x32_s5_w8_pp"),
+    info_of<K29>("256x128x32_s5_w8_m16_pp"),
 };
 
 template <class C>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(gemm_tiled_kernel<C>, dim3(p.s.grid), dim3(C::THREADS), 0, stream, p);
+  if constexpr (C::PP)
+    hipLaunchKernelGGL(gemm_pingpong_kernel<C>, dim3(p.s.grid), dim3(C::THREADS), 0, stream, p);
+  else
+    hipLaunchKernelGGL(gemm_tiled_kernel<C>, dim3(p.s.grid), dim3(C::THREADS), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.s.mode == MODE_DATA_PARALLEL) return e;
   // Slices per tile: enough workgroups to cover the CUs, at least 4 KiB each.
@@ -746,9 +892,12 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t stream) {
 template <class C>
 int32_t occupancy_cfg() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_tiled_kernel<C>, C::THREADS, 0) !=
-      hipSuccess)
-    return 0;
+  hipError_t e;
+  if constexpr (C::PP)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_pingpong_kernel<C>, C::THREADS, 0);
+  else
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_tiled_kernel<C>, C::THREADS, 0);
+  if (e != hipSuccess) return 0;
   return n;
 }
 

@@ -247,8 +247,9 @@ def test_subnormal_inputs():
 
 # --- every kernel variant and schedule mode ---------------------------------
 
-# Tiled kernel ids 0-9 use v_mfma_f32_32x32x16_f16, 10-24 v_mfma_f32_16x16x32_f16.
-PLANS = [f"kid={k}" for k in range(25)] + [
+# Tiled kernel ids 0-9 use v_mfma_f32_32x32x16_f16, 10-24 v_mfma_f32_16x16x32_f16;
+# 25-29 run the ping-pong main loop (28 with the 32x32x16 MFMA).
+PLANS = [f"kid={k}" for k in range(30)] + [
     "kid=0,mode=1,splits=3", "kid=0,mode=2", "kid=0,mode=2,grid=37",
     "kid=4,mode=2,grid=100", "kid=6,mode=1,splits=5", "kid=2,mode=2,grid=64",
     "kid=1,mode=1,splits=2", "kid=3,mode=2,grid=29", "kid=5,mode=2,grid=130",
@@ -257,6 +258,8 @@ PLANS = [f"kid={k}" for k in range(25)] + [
     "kid=11,mode=1,splits=2", "kid=19,mode=2", "kid=16,mode=1,splits=3,grid=40",
     "kid=14,mode=2,grid=64", "kid=18,mode=1,splits=5", "kid=20,mode=1,splits=3",
     "kid=21,mode=2,grid=37", "kid=22,mode=2", "kid=24,mode=1,splits=2",
+    "kid=25,mode=1,splits=3", "kid=26,mode=2,grid=37", "kid=27,mode=2",
+    "kid=28,mode=1,splits=2,grid=40", "kid=29,mode=2,grid=29",
 ]
 
 
@@ -275,7 +278,7 @@ def test_forced_plans(plan, monkeypatch):
     assert_tol(run(A, B), ref, S, f"{plan} uniform")
 
 
-@pytest.mark.parametrize("kid", [0, 7, 10, 11, 12, 19, 20, 22, 23])
+@pytest.mark.parametrize("kid", [0, 7, 10, 11, 12, 19, 20, 22, 23, 25, 27, 29])
 @pytest.mark.parametrize("K", [24, 72, 200])
 def test_forced_plans_short_k(kid, K, monkeypatch):
     """K of one to a few k-tiles, odd and even counts (one k-step per stage
