@@ -492,7 +492,7 @@ __device__ __forceinline__ void write_partial(f32x4* part,
                          acc[i][j][4 * g + 3]};
         __builtin_amdgcn_raw_buffer_store_b128(
             __builtin_bit_cast(u32x4, v), r, voff, ((i * C::FN + j) * G + g) * C::WAVES * 64 * 16,
-            0);
+            0);  // cached: the reduce pass reads the partials right back
       }
 }
 
@@ -567,12 +567,16 @@ __device__ __forceinline__ void epilogue(const GemmParams& p,
         const int n = n_base + j * C::M::DIM + C::M::acc_n(g, lane);
         const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                          acc[i][j][4 * g + 3]};
+        // Non-temporal: C is written once and not read back, and the
+        // workgroups of an XCD together write more C per round of tiles than
+        // its L2 holds, which would otherwise push out the A and B panels
+        // the next round reads.
         if (full && p.c_vec4) {
-          *reinterpret_cast<f32x4*>(crow + n) = v;
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(crow + n));
         } else if (m < p.M) {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            if (n + q < p.N) crow[n + q] = v[q];
+            if (n + q < p.N) __builtin_nontemporal_store(v[q], crow + n + q);
         }
       }
     }
