@@ -38,11 +38,17 @@ METRIC = ("TFLOP/s and µs/call per M×N×K (fp16→fp32 A·Bᵀ); "
           "% of MI355X MFMA peak")
 PEAK_TFLOPS = 2500.0         # MI355X dense fp16 MFMA (published)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E (published)
-# The pages' own number for this workload (one B200): 553.1 - 554.3 us at 8192^3.
+# The pages' own numbers (one B200, "SASS-Level Kernel Generation for Blackwell",
+# section "The numbers"): midpoints of the ranges, in us per call. Context only.
 PAGE_US = {"8192^3": (553.1 + 554.3) / 2, "1024^3": (4.64 + 4.67) / 2,
-           "2048x2048x16384": (73.92 + 74.11) / 2, "1024x1024x65536": (76.93 + 77.22) / 2}
+           "2048x2048x16384": (73.92 + 74.11) / 2, "1024x1024x65536": (76.93 + 77.22) / 2,
+           "1536^3": 7.87, "2048^3": 14.46, "3072x1280x2048": 14.08, "4096x4096x1024": 26.11,
+           "4096^3": (75.78 + 75.97) / 2, "8192x2048x4096": (75.84 + 75.97) / 2,
+           "16384^3": (4132.8 + 4239.4) / 2}
+# Timed calls per shape, as the pages time them ("How we measured").
 CALLS = {"256^3": 400, "1024^3": 400, "2048x2048x16384": 200, "1024x1024x65536": 200,
-         "8192^3": 40}
+         "8192^3": 40, "1536^3": 400, "2048^3": 400, "3072x1280x2048": 400,
+         "4096x4096x1024": 300, "4096^3": 200, "8192x2048x4096": 200, "16384^3": 12}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -260,13 +266,17 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="8192^3")
+    ap.add_argument("--workload", default="8192^3",
+                    help="one of the five workloads, or one of the pages' other shapes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shapes", action="store_true",
                     help="also time the five workloads, each call alone")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB fp32 copy kernel (counter calibration)")
-    ap.add_argument("--sweeps", type=int, default=2, help="forward/reverse sweeps for shapes")
+    ap.add_argument("--sweeps", type=int, default=4,
+                    help="sweeps over the shapes, alternately forward and reverse")
+    ap.add_argument("--page-shapes", action="store_true",
+                    help="with --shapes, also time the other shapes of the pages' table")
     ap.add_argument("--vendor", action="store_true",
                     help="also time hipBLASLt's fastest exact algorithm on every workload "
                          "(context only)")
@@ -292,7 +302,11 @@ def main():
     torch.cuda.set_device(dev)
 
     name = args.workload
-    M, N, K = inputs.WORKLOADS[name]
+    all_shapes = {**inputs.WORKLOADS, **inputs.PAGE_SHAPES}
+    if name not in all_shapes:
+        print(f"unknown workload {name!r}; known: {', '.join(all_shapes)}", file=sys.stderr)
+        sys.exit(2)
+    M, N, K = all_shapes[name]
     flops, nbytes = algorithmic(M, N, K)
     log(f"[bench] workload {name}: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
     A, B, At, Bt = make_device_operands(torch, (M, N, K), dev)
@@ -313,12 +327,15 @@ def main():
 
     shapes = []
     if args.shapes:
-        names = list(inputs.WORKLOADS)
+        table = dict(inputs.WORKLOADS)
+        if args.page_shapes:
+            table.update(inputs.PAGE_SHAPES)
+        names = list(table)
         results = {n: [] for n in names}
         for sweep in range(args.sweeps):
             order = names if sweep % 2 == 0 else names[::-1]
             for n in order:
-                m, nn, k = inputs.WORKLOADS[n]
+                m, nn, k = table[n]
                 if n == name:
                     a, b = At, Bt
                     c = C
@@ -331,7 +348,7 @@ def main():
                 del a, b, c
                 torch.cuda.empty_cache()
         for n in names:
-            m, nn, k = inputs.WORKLOADS[n]
+            m, nn, k = table[n]
             f, by = algorithmic(m, nn, k)
             lo, hi = min(results[n]), max(results[n])
             mid = (lo + hi) / 2

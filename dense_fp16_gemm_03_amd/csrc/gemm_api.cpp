@@ -109,8 +109,9 @@ bool tiled_eligible(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
 //     persistent grid walking the tiles by stride;
 //   * fewer tiles but long K (>= 128 k-steps of 32): the same tiles with K
 //     split so tiles x splits fills the CUs (each share keeps >= 64 k-steps);
-//   * small problems: 128x128 tiles (64x64 when there are fewer than 16 of
-//     them), data-parallel; the splits' reduce pass costs more than it gains.
+//   * smaller problems: 128x128 tiles, or 64x64 tiles when 128x128 ones
+//     would fill fewer than half the CUs, data-parallel (at these sizes the
+//     reduce pass of a split costs more than it gains).
 Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                int64_t ldb, const float* C, int64_t ldc, int32_t cus) {
   Plan plan;
@@ -133,7 +134,8 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
       splits = (int32_t)std::max<int64_t>(sp, 1);
       mode = splits > 1 ? MODE_SPLIT : MODE_DATA_PARALLEL;
     } else {
-      kid = cdiv(M, 128) * cdiv(N, 128) >= 16 ? KID_128x128x64_S4_W4 : KID_64x64x64_S4_W4;
+      kid = 2 * cdiv(M, 128) * cdiv(N, 128) >= cus ? KID_128x128x64_S4_W4_M16
+                                                    : KID_64x64x64_S4_W4_M16;
     }
   }
   if (o.kid >= 0 && kernel_info(o.kid)) kid = o.kid;

@@ -47,12 +47,17 @@ namespace g16 {
   X(26, KID_256x256x32_S4_W8_M16_PP, 256, 256, 32, 4, 2, 4, 16, 0, 1) \
   X(27, KID_256x256x32_S3_W8_M16_PP, 256, 256, 32, 3, 2, 4, 16, 0, 1) \
   X(28, KID_256x256x32_S5_W8_PP, 256, 256, 32, 5, 2, 4, 32, 0, 1)     \
-  X(29, KID_256x128x32_S5_W8_M16_PP, 256, 128, 32, 5, 2, 4, 16, 0, 1)
+  X(29, KID_256x128x32_S5_W8_M16_PP, 256, 128, 32, 5, 2, 4, 16, 0, 1) \
+  X(30, KID_64x64x64_S8_W4_M16, 64, 64, 64, 8, 2, 2, 16, 0, 0)         \
+  X(31, KID_64x64x32_S10_W4_M16, 64, 64, 32, 10, 2, 2, 16, 0, 0)       \
+  X(32, KID_128x64x64_S6_W4_M16, 128, 64, 64, 6, 2, 2, 16, 0, 0)       \
+  X(33, KID_64x64x64_S8_W4, 64, 64, 64, 8, 2, 2, 32, 0, 0)             \
+  X(34, KID_128x128x64_S4_W4_M16_RS, 128, 128, 64, 4, 2, 2, 16, 1, 0)
 
 #define G16_KID_ENUM(id, name, ...) name = id,
 enum KernelId : int32_t {
   G16_TILED_KERNELS(G16_KID_ENUM)
-  KID_COUNT = 30,
+  KID_COUNT = 35,
   KID_GENERAL = 100  // any shape and alignment, 64 x 64 tiles, no LDS
 };
 #undef G16_KID_ENUM

@@ -873,6 +873,9 @@ constexpr KernelInfo kInfos[KID_COUNT] = {
     info_of<K25>("256x256x32_s5_w8_m16_pp"), info_of<K26>("256x256x32_s4_w8_m16_pp"),
     info_of<K27>("256x256x32_s3_w8_m16_pp"), info_of<K28>("256x256x32_s5_w8_pp"),
     info_of<K29>("256x128x32_s5_w8_m16_pp"),
+    info_of<K30>("64x64x64_s8_w4_m16"),      info_of<K31>("64x64x32_s10_w4_m16"),
+    info_of<K32>("128x64x64_s6_w4_m16"),     info_of<K33>("64x64x64_s8_w4"),
+    info_of<K34>("128x128x64_s4_w4_m16_rs"),
 };
 
 template <class C>

@@ -34,6 +34,19 @@ WORKLOADS = {
     "8192^3": (8192, 8192, 8192),
 }
 
+# The other shapes of the timing table in "SASS-Level Kernel Generation for
+# Blackwell" (section "The numbers"): same operation, timed and checked here
+# as extra cases.
+PAGE_SHAPES = {
+    "1536^3": (1536, 1536, 1536),
+    "2048^3": (2048, 2048, 2048),
+    "3072x1280x2048": (3072, 1280, 2048),
+    "4096x4096x1024": (4096, 4096, 1024),
+    "4096^3": (4096, 4096, 4096),
+    "8192x2048x4096": (8192, 2048, 4096),
+    "16384^3": (16384, 16384, 16384),
+}
+
 
 def uniform(rows: int, cols: int, seed: int) -> np.ndarray:
     """rows x cols binary16, i.i.d. uniform on [-1, 1]."""

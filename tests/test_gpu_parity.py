@@ -153,6 +153,23 @@ def test_workload_parity(name, kind):
         assert_tol(g, ref, S, f"{name} uniform")
 
 
+@pytest.mark.parametrize("name", list(inputs.PAGE_SHAPES))
+def test_page_shape_parity(name):
+    """The other shapes of the pages' timing table, integer inputs, bit-exact
+    (sampled rows, columns and points where the full reference is too slow)."""
+    M, N, K = inputs.PAGE_SHAPES[name]
+    A, B = operands((M, N, K), "integer")
+    log(f"  plan: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
+    got = run(A, B)
+    if M * N * K <= 2048 ** 3:
+        ref, _ = oracle.gemm_abt(A, B)
+        assert_exact(got, ref, f"{name} integer")
+    else:
+        rows, cols = sample_points(M, N, n_rand=2000)
+        ref, _ = oracle.gemm_abt_elems(A, B, rows, cols)
+        assert_exact(got[rows, cols], ref, f"{name} integer")
+
+
 def test_hash_int_inputs():
     """Integers in [-3, 3] from a hash of the index: exact."""
     M, N, K = 1024, 1024, 4096
@@ -248,8 +265,9 @@ def test_subnormal_inputs():
 # --- every kernel variant and schedule mode ---------------------------------
 
 # Tiled kernel ids 0-9 use v_mfma_f32_32x32x16_f16, 10-24 v_mfma_f32_16x16x32_f16;
-# 25-29 run the ping-pong main loop (28 with the 32x32x16 MFMA).
-PLANS = [f"kid={k}" for k in range(30)] + [
+# 25-29 run the ping-pong main loop (28 with the 32x32x16 MFMA); 30-34 are
+# small tiles with deep rings.
+PLANS = [f"kid={k}" for k in range(35)] + [
     "kid=0,mode=1,splits=3", "kid=0,mode=2", "kid=0,mode=2,grid=37",
     "kid=4,mode=2,grid=100", "kid=6,mode=1,splits=5", "kid=2,mode=2,grid=64",
     "kid=1,mode=1,splits=2", "kid=3,mode=2,grid=29", "kid=5,mode=2,grid=130",
@@ -260,6 +278,7 @@ PLANS = [f"kid={k}" for k in range(30)] + [
     "kid=21,mode=2,grid=37", "kid=22,mode=2", "kid=24,mode=1,splits=2",
     "kid=25,mode=1,splits=3", "kid=26,mode=2,grid=37", "kid=27,mode=2",
     "kid=28,mode=1,splits=2,grid=40", "kid=29,mode=2,grid=29",
+    "kid=30,mode=1,splits=3", "kid=31,mode=2,grid=37", "kid=32,mode=2",
 ]
 
 
@@ -278,7 +297,7 @@ def test_forced_plans(plan, monkeypatch):
     assert_tol(run(A, B), ref, S, f"{plan} uniform")
 
 
-@pytest.mark.parametrize("kid", [0, 7, 10, 11, 12, 19, 20, 22, 23, 25, 27, 29])
+@pytest.mark.parametrize("kid", [0, 7, 10, 11, 12, 19, 20, 22, 23, 25, 27, 29, 30, 31])
 @pytest.mark.parametrize("K", [24, 72, 200])
 def test_forced_plans_short_k(kid, K, monkeypatch):
     """K of one to a few k-tiles, odd and even counts (one k-step per stage
