@@ -21,7 +21,7 @@ using namespace g16;
 constexpr int32_t kDefaultCUs = 256;  // MI355X: 8 XCDs x 32 CUs
 // Kernel for large squares and for long K: 256x256 tiles, 16x16x32 MFMA,
 // two waves per SIMD in the ping-pong main loop.
-constexpr int32_t KID_LARGE = KID_256x256x32_S5_W8_M16_PP;
+constexpr int32_t KID_LARGE = KID_256x256x32_S3_W8_M16_PP;
 
 struct Plan {
   int32_t kid = -1;       // tiled kernel id, KID_GENERAL, or -1 (nothing to do)

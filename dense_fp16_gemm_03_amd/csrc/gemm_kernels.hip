@@ -49,6 +49,11 @@ constexpr uint32_t kMaskedOffset = 0x80000000u;
 constexpr int32_t kNumRecords = 0x7FFFFFF0;
 constexpr int32_t kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kReduceThreads = 256;
+// Buffer-store cache policy for C in the ping-pong kernels: streaming and
+// write-through to the system coherence point (nt sc1). Their rounds of
+// 256x256 tiles write tens of MiB of C at once; measured faster than
+// streaming stores alone.
+constexpr int kStoreNtSc1 = 2 | 16;
 
 // The two fp16 MFMA shapes with fp32 accumulation on gfx950. Both take 8
 // halves of each operand per lane; the B tile is the first operand and the A
@@ -551,6 +556,9 @@ __device__ __forceinline__ void reduce_range(const GemmParams& p, const f32x4* p
 // Write the wave's accumulators to C (a tile computed by one unit alone).
 // Lane l holds, for block (i, j) and register v = 4g + q, row
 // m_base + DIM i + acc_m(l) and column n_base + DIM j + acc_n(g, l) + q.
+// Non-temporal: C is written once and not read back, and the workgroups of
+// an XCD together write more C per round of tiles than its L2 holds, which
+// would otherwise push out the A and B panels the next round reads.
 template <class C>
 __device__ __forceinline__ void epilogue(const GemmParams& p,
                                          const typename C::acc_t (&acc)[C::FM][C::FN],
@@ -567,10 +575,6 @@ __device__ __forceinline__ void epilogue(const GemmParams& p,
         const int n = n_base + j * C::M::DIM + C::M::acc_n(g, lane);
         const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                          acc[i][j][4 * g + 3]};
-        // Non-temporal: C is written once and not read back, and the
-        // workgroups of an XCD together write more C per round of tiles than
-        // its L2 holds, which would otherwise push out the A and B panels
-        // the next round reads.
         if (full && p.c_vec4) {
           __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(crow + n));
         } else if (m < p.M) {
@@ -578,6 +582,53 @@ __device__ __forceinline__ void epilogue(const GemmParams& p,
           for (int q = 0; q < 4; ++q)
             if (n + q < p.N) __builtin_nontemporal_store(v[q], crow + n + q);
         }
+      }
+    }
+  }
+}
+
+// Store instructions one wave's epilogue_stream issues on its vector path
+// (16-byte stores of 4 consecutive columns from every accumulator group).
+template <class C>
+constexpr int epilogue_stores() {
+  return C::FM * C::FN * C::M::GROUPS;
+}
+
+// True when the wave's block of C takes the vector path of epilogue_stream:
+// all of it inside C, 16-byte aligned rows, and byte offsets within the
+// block below 2^31. Uniform across the wave.
+template <class C>
+__device__ __forceinline__ bool epilogue_vector(const GemmParams& p, int m_base, int n_base) {
+  return m_base + C::WM <= p.M && n_base + C::WN <= p.N && p.c_vec4 &&
+         (int64_t)C::WM * p.ldc * 4 < ((int64_t)1 << 31);
+}
+
+// epilogue() for the ping-pong kernels: on the vector path every group of 4
+// goes out as one 16-byte buffer store (exactly epilogue_stores<C>()
+// instructions, which the next unit's first stage waits count on) with the
+// nt sc1 policy; ragged blocks fall back to epilogue().
+template <class C>
+__device__ __forceinline__ void epilogue_stream(const GemmParams& p,
+                                                const typename C::acc_t (&acc)[C::FM][C::FN],
+                                                int m_base, int n_base, int lane) {
+  if (!epilogue_vector<C>(p, m_base, n_base)) {
+    epilogue<C>(p, acc, m_base, n_base, lane);
+    return;
+  }
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.C + (int64_t)m_base * p.ldc + n_base), (short)0, kNumRecords, kBufferWord3);
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    const int row = i * C::M::DIM + C::M::acc_m(lane);
+#pragma unroll
+    for (int g = 0; g < C::M::GROUPS; ++g) {
+      const int voff = (row * (int)p.ldc + C::M::acc_n(g, lane)) * 4;
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                         acc[i][j][4 * g + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rc, voff,
+                                               j * C::M::DIM * 4, kStoreNtSc1);
       }
     }
   }
@@ -667,6 +718,34 @@ void gemm_tiled_kernel(GemmParams p) {
   }
 }
 
+// Per-unit state of the load stream: operand windows, per-lane load map and
+// k range of one unit (output tile, or share of one).
+template <class C>
+struct UnitLoads {
+  Operands op;
+  LoadMap<C, C::A_LOADS> ma;
+  LoadMap<C, C::B_LOADS> mb;
+  int m0, n0, k_begin, nk;
+};
+
+template <class C>
+__device__ __forceinline__ void unit_loads(const GemmParams& p, const Segment& seg, int wave,
+                                           int lane, UnitLoads<C>& u) {
+  u.m0 = seg.tm * C::BM;
+  u.n0 = seg.tn * C::BN;
+  u.k_begin = seg.k_begin;
+  u.nk = seg.k_end - seg.k_begin;
+  // Loads cover this unit's k range only; the stages past its end that the
+  // ring still issues are fully masked (zero-filled, no memory access).
+  const int k_limit = min_of(p.K, seg.k_end * C::BK);
+  u.op.ra = __builtin_amdgcn_make_buffer_rsrc((void*)(p.A + (int64_t)u.m0 * p.lda), (short)0,
+                                              kNumRecords, kBufferWord3);
+  u.op.rb = __builtin_amdgcn_make_buffer_rsrc((void*)(p.B + (int64_t)u.n0 * p.ldb), (short)0,
+                                              kNumRecords, kBufferWord3);
+  make_load_map<C, C::A_LOADS>(u.ma, wave, lane, p.M - u.m0, p.lda, k_limit);
+  make_load_map<C, C::B_LOADS>(u.mb, wave, lane, p.N - u.n0, p.ldb, k_limit);
+}
+
 // Ping-pong main loop (8 waves, two per SIMD). The waves form two groups,
 // one wave of each on every SIMD (group 0: waves 0-3, group 1: waves 4-7),
 // and group 1 runs one phase behind group 0. A stage takes two phases per
@@ -685,12 +764,26 @@ void gemm_tiled_kernel(GemmParams p) {
 // a barrier) and later; stage j + 1 is complete in LDS before either group
 // reads it, since every wave waits for its share of it before the barrier
 // that opens group 0's memory phase j + 1.
+//
+// Between units, each wave issues the first STAGES - 1 stages of its next
+// unit as soon as its last compute phase is done (no wave reads the ring
+// any more by then: group 1's last reads end before the barrier that closes
+// group 0's last compute phase), and only then the stores of the finished
+// unit. The next unit's first STAGES - 2 stage waits leave those stores
+// in flight (their count is exact on the epilogue's vector path and for
+// partial tiles), so the write of C overlaps the start of the next unit
+// instead of stalling it: vector-memory operations retire in issue order,
+// and the stores are younger than every stage waited for until stage
+// STAGES - 1, which is issued after them.
 template <class C>
 __global__ __launch_bounds__(C::THREADS)
 __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_EU, C::WAVES_PER_EU)))
 void gemm_pingpong_kernel(GemmParams p) {
   static_assert(C::WAVES == 8, "ping-pong pairs two waves per SIMD");
   static_assert(C::STAGES >= 3, "a stage is awaited while the next two are in flight");
+  constexpr int kStage = C::LOADS * (C::STAGES - 2);  // loads younger than an awaited stage
+  constexpr int kStores = epilogue_stores<C>();
+  static_assert(kStage + kStores <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -702,55 +795,50 @@ void gemm_pingpong_kernel(GemmParams p) {
   const int v = virtual_wg(blockIdx.x, p.s.grid, p.s.xcd_remap);
 
   Segment seg;
-  for (int n = 0; seg_at_uniform(p.s, v, n, &seg); ++n) {
-    const int m0 = seg.tm * C::BM;
-    const int n0 = seg.tn * C::BN;
-    const int nk = seg.k_end - seg.k_begin;
-    const int k_limit = min_of(p.K, seg.k_end * C::BK);
+  if (!seg_at_uniform(p.s, v, 0, &seg)) return;
+  UnitLoads<C> u;
+  unit_loads<C>(p, seg, wave, lane, u);
+#pragma unroll
+  for (int s = 0; s < C::STAGES - 1; ++s) {
+#pragma unroll
+    for (int j = 0; j < C::LOADS; ++j)
+      issue_one<C>(j, smem + s * C::STAGE_BYTES, u.op, u.ma, u.mb, wave, (u.k_begin + s) * C::BK);
+  }
+  // True when the previous unit's kStores stores were issued after this
+  // unit's first stages (so they may stay in flight through its first
+  // STAGES - 2 stage waits).
+  bool stores_behind = false;
 
-    Operands op;
-    op.ra = __builtin_amdgcn_make_buffer_rsrc((void*)(p.A + (int64_t)m0 * p.lda), (short)0,
-                                              kNumRecords, kBufferWord3);
-    op.rb = __builtin_amdgcn_make_buffer_rsrc((void*)(p.B + (int64_t)n0 * p.ldb), (short)0,
-                                              kNumRecords, kBufferWord3);
-    LoadMap<C, C::A_LOADS> ma;
-    LoadMap<C, C::B_LOADS> mb;
-    make_load_map<C, C::A_LOADS>(ma, wave, lane, p.M - m0, p.lda, k_limit);
-    make_load_map<C, C::B_LOADS>(mb, wave, lane, p.N - n0, p.ldb, k_limit);
-
+  for (int n = 0;; ++n) {
     typename C::acc_t acc[C::FM][C::FN];
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) acc[i][j] = typename C::acc_t{};
 
-    // The previous unit's loads have landed and all LDS reads are done.
-    wait_vm<0>();
-    wait_lgkm_zero();
-    lds_barrier();
-#pragma unroll
-    for (int s = 0; s < C::STAGES - 1; ++s) {
-#pragma unroll
-      for (int j = 0; j < C::LOADS; ++j)
-        issue_one<C>(j, smem + s * C::STAGE_BYTES, op, ma, mb, wave, (seg.k_begin + s) * C::BK);
-    }
-    wait_vm<C::LOADS * (C::STAGES - 2)>();
+    if (stores_behind)
+      wait_vm<kStage + kStores>();
+    else
+      wait_vm<kStage>();
     phase_barrier();
     if (late) phase_barrier();  // group 1 starts one phase behind
 
     Frags<C> fr[C::KSTEPS];
     int st = 0;
-    for (int it = 0; it < nk; ++it) {
+    for (int it = 0; it < u.nk; ++it) {
       const int st_load = st == 0 ? C::STAGES - 1 : st - 1;
       const char* stage = smem + st * C::STAGE_BYTES;
       // Memory phase.
 #pragma unroll
       for (int ks = 0; ks < C::KSTEPS; ++ks) read_frags<C>(stage, ks, wm, wn, lane, fr[ks]);
-      const int k0 = (seg.k_begin + it + C::STAGES - 1) * C::BK;
+      const int k0 = (u.k_begin + it + C::STAGES - 1) * C::BK;
 #pragma unroll
       for (int j = 0; j < C::LOADS; ++j)
-        issue_one<C>(j, smem + st_load * C::STAGE_BYTES, op, ma, mb, wave, k0);
-      wait_vm<C::LOADS * (C::STAGES - 2)>();
+        issue_one<C>(j, smem + st_load * C::STAGE_BYTES, u.op, u.ma, u.mb, wave, k0);
+      if (stores_behind && it < C::STAGES - 2)
+        wait_vm<kStage + kStores>();
+      else
+        wait_vm<kStage>();
       wait_lgkm_zero();
       phase_barrier();
       // Compute phase.
@@ -765,15 +853,37 @@ void gemm_pingpong_kernel(GemmParams p) {
       st = st + 1 == C::STAGES ? 0 : st + 1;
     }
 
-    // Group 0 finishes while group 1 runs its last compute phase, then
-    // passes the barrier that matches group 1's extra one.
-    if (seg.role == ROLE_ONLY) {
-      epilogue<C>(p, acc, m0 + wm * C::WM, n0 + wn * C::WN, lane);
+    // Group 0 is here while group 1 runs its last compute phase; group 1
+    // follows one phase later. The loads still in flight are the masked
+    // tail stages (no memory access): let them land before the ring is
+    // refilled, then start the next unit's stream.
+    const Segment done = seg;
+    const int m_base = u.m0 + wm * C::WM;
+    const int n_base = u.n0 + wn * C::WN;
+    const bool more = seg_at_uniform(p.s, v, n + 1, &seg);
+    if (more) {
+      wait_vm<0>();
+      unit_loads<C>(p, seg, wave, lane, u);
+#pragma unroll
+      for (int s = 0; s < C::STAGES - 1; ++s) {
+#pragma unroll
+        for (int j = 0; j < C::LOADS; ++j)
+          issue_one<C>(j, smem + s * C::STAGE_BYTES, u.op, u.ma, u.mb, wave,
+                       (u.k_begin + s) * C::BK);
+      }
+    }
+    if (done.role == ROLE_ONLY) {
+      stores_behind = more && epilogue_vector<C>(p, m_base, n_base);
+      epilogue_stream<C>(p, acc, m_base, n_base, lane);
     } else {
-      write_partial<C>(p.partials + ((int64_t)seg.tile * p.s.slots + seg.index) * (C::BM * C::BN / 4),
+      // write_partial issues epilogue_stores<C>() buffer stores as well.
+      stores_behind = more;
+      write_partial<C>(p.partials + ((int64_t)done.tile * p.s.slots + done.index) * (C::BM * C::BN / 4),
                        acc, wave, lane);
     }
+    // Matches group 1's extra barrier at the start of the unit.
     if (!late) phase_barrier();
+    if (!more) break;
   }
 }
 

@@ -279,6 +279,11 @@ PLANS = [f"kid={k}" for k in range(35)] + [
     "kid=25,mode=1,splits=3", "kid=26,mode=2,grid=37", "kid=27,mode=2",
     "kid=28,mode=1,splits=2,grid=40", "kid=29,mode=2,grid=29",
     "kid=30,mode=1,splits=3", "kid=31,mode=2,grid=37", "kid=32,mode=2",
+    # Several units per workgroup: the ping-pong kernels start the next unit's
+    # loads before the previous unit's stores, mixing full tiles (vector
+    # stores left in flight) with ragged ones (element stores).
+    "kid=25,grid=2", "kid=26,grid=3", "kid=27,grid=3", "kid=27,grid=1",
+    "kid=27,mode=1,splits=2,grid=7", "kid=28,grid=4", "kid=29,grid=5",
 ]
 
 
@@ -310,6 +315,23 @@ def test_forced_plans_short_k(kid, K, monkeypatch):
     A, B = inputs.uniform(M, K, 153), inputs.uniform(N, K, 154)
     ref, S = oracle.gemm_abt(A, B)
     assert_tol(run(A, B), ref, S, f"kid={kid} K={K} uniform")
+
+
+@pytest.mark.parametrize("plan", ["kid=25,grid=1", "kid=26,grid=2", "kid=27,grid=1",
+                                  "kid=27,mode=1,splits=2,grid=3"])
+@pytest.mark.parametrize("K", [24, 72, 200])
+def test_forced_plans_short_units(plan, K, monkeypatch):
+    """Many short units per workgroup: units of one to a few k-tiles follow
+    each other while the previous unit's stores may still be in flight."""
+    monkeypatch.setenv("GEMM_F16_PLAN", plan)
+    M, N = 776, 520
+    log(f"  plan: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
+    Ai, Bi = inputs.integer(M, K, 155), inputs.integer(N, K, 156)
+    ref, _ = oracle.gemm_abt(Ai, Bi)
+    assert_exact(run(Ai, Bi), ref, f"{plan} K={K} integer")
+    A, B = inputs.uniform(M, K, 157), inputs.uniform(N, K, 158)
+    ref, S = oracle.gemm_abt(A, B)
+    assert_tol(run(A, B), ref, S, f"{plan} K={K} uniform")
 
 
 # --- invariants -------------------------------------------------------------
