@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of C = A * B^T (fp16 in, fp32 accumulate/out) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8192^3]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8192^3] [--dtype f16|bf16]
                     [--no-cpu-baseline] [--shapes] [--vendor] [--calibrate-copy]
 
 A step is one call of gemm_f16_f32_abt through the C ABI on synthetic
@@ -31,6 +31,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -72,11 +74,18 @@ def algorithmic(M, N, K):
     return flops, nbytes
 
 
-def make_device_operands(torch, shape, dev):
+def make_device_operands(torch, shape, dev, dtype="f16"):
+    """Host operands (float16, or uint16 bfloat16 bits) and their device copies."""
     from dense_fp16_gemm_03_amd import inputs
 
-    A, B = inputs.workload_operands(shape, "uniform")
-    return A, B, torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+    A, B = inputs.workload_operands(shape, "uniform", dtype)
+    if dtype == "bf16":
+        def dev_t(x):
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        def dev_t(x):
+            return torch.from_numpy(x).to(dev)
+    return A, B, dev_t(A), dev_t(B)
 
 
 def time_throughput(torch, gemm, At, Bt, C, steps, warmup):
@@ -116,19 +125,19 @@ def time_calls_alone(torch, gemm, At, Bt, C, calls, warmup=20):
 
 
 def cpu_baseline(A, B, M, N, K, budget_s=25.0):
-    import numpy as np
-
     import oracle
+
+    ref = oracle.gemm_abt_bf16 if A.dtype == np.uint16 else oracle.gemm_abt
 
     threads = oracle.default_threads()
     rows = max(1, threads)
     t0 = time.perf_counter()
-    oracle.gemm_abt(A[:rows], B, threads=threads)
+    ref(A[:rows], B, threads=threads)
     t = time.perf_counter() - t0
     est = t / rows
     rows2 = int(min(M, max(rows, budget_s / max(est, 1e-9))))
     t0 = time.perf_counter()
-    oracle.gemm_abt(A[:rows2], B, threads=threads)
+    ref(A[:rows2], B, threads=threads)
     t = time.perf_counter() - t0
     flops = 2.0 * rows2 * N * K
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
@@ -267,6 +276,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--dtype", default="f16", choices=("f16", "bf16"),
+                    help="operand type: binary16 (the workloads' type) or bfloat16")
     ap.add_argument("--workload", default="8192^3",
                     help="one of the five workloads, or one of the pages' other shapes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -310,7 +321,7 @@ def main():
     M, N, K = all_shapes[name]
     flops, nbytes = algorithmic(M, N, K)
     log(f"[bench] workload {name}: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
-    A, B, At, Bt = make_device_operands(torch, (M, N, K), dev)
+    A, B, At, Bt = make_device_operands(torch, (M, N, K), dev, args.dtype)
     C = torch.empty((M, N), dtype=torch.float32, device=dev)
 
     elapsed, kernel_ms = time_throughput(torch, gemm, At, Bt, C, args.steps, args.warmup)
@@ -320,7 +331,8 @@ def main():
     achieved = flops / avg_kernel_s / 1e12
     log(f"[bench] {args.steps} steps in {elapsed * 1e3:.2f} ms: {value:.1f} TFLOP/s; "
         f"kernel avg {avg_kernel_s * 1e6:.2f} us ({achieved:.1f} TFLOP/s)")
-    traffic = traffic_for(name, avg_kernel_s)
+    # committed counters are for the binary16 path
+    traffic = traffic_for(name, avg_kernel_s) if args.dtype == "f16" else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
                 "kernel_avg_us": round(avg_kernel_s * 1e6, 3),
@@ -341,7 +353,7 @@ def main():
                     a, b = At, Bt
                     c = C
                 else:
-                    _, _, a, b = make_device_operands(torch, (m, nn, k), dev)
+                    _, _, a, b = make_device_operands(torch, (m, nn, k), dev, args.dtype)
                     c = torch.empty((m, nn), dtype=torch.float32, device=dev)
                 us = time_calls_alone(torch, gemm, a, b, c, CALLS[n])
                 results[n].append(us)
@@ -376,13 +388,13 @@ def main():
         log(f"[bench] cpu: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
 
     vs = None
-    if name in PAGE_US:
+    if name in PAGE_US and args.dtype == "f16":  # the pages time binary16 only
         vs = round(value / (flops / (PAGE_US[name] * 1e-6) / 1e12), 4)
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": vs, "dtype": "f16",
-        "data": "synthetic: uniform[-1,1] fp16, seeds 1 (A) and 2 (B), resident in HBM",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": vs, "dtype": args.dtype,
+        "data": f"synthetic: uniform[-1,1] {args.dtype}, seeds 1 (A) and 2 (B), resident in HBM",
         "config": {"workload": f"gemm_abt {M}x{N}x{K}", "M": M, "N": N, "K": K,
                    "accumulate": "f32", "output": "f32",
                    "plan": gemm.gemm_f16_f32_abt_describe(M, N, K),

@@ -113,7 +113,7 @@ bool tiled_eligible(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
 //     would fill fewer than half the CUs, data-parallel (at these sizes the
 //     reduce pass of a split costs more than it gains).
 Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-               int64_t ldb, const float* C, int64_t ldc, int32_t cus) {
+               int64_t ldb, const float* C, int64_t ldc, int32_t cus, int32_t dt = DT_F16) {
   Plan plan;
   if (M == 0 || N == 0) return plan;
   plan.c_vec4 = ((uintptr_t)C % 16 == 0) && (ldc % 4 == 0);
@@ -138,7 +138,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
                                                     : KID_64x64x64_S4_W4_M16;
     }
   }
-  if (o.kid >= 0 && kernel_info(o.kid)) kid = o.kid;
+  if (o.kid >= 0 && kernel_info(o.kid) && tiled_has(o.kid, dt)) kid = o.kid;
   if (o.mode >= 0 && o.mode <= MODE_STREAM_K) mode = o.mode;
   if (o.splits >= 1) splits = o.splits;
 
@@ -244,9 +244,9 @@ gemm_status_t library_workspace(int dev, hipStream_t stream, size_t need, void**
   return GEMM_OK;
 }
 
-gemm_status_t run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-                  int64_t ldb, float* C, int64_t ldc, bool caller_ws, void* ws, size_t ws_bytes,
-                  void* stream_v) {
+gemm_status_t run(int32_t dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                  const void* B, int64_t ldb, float* C, int64_t ldc, bool caller_ws, void* ws,
+                  size_t ws_bytes, void* stream_v) {
   gemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc);
   if (st != GEMM_OK) return st;
   if (M == 0 || N == 0) return GEMM_OK;
@@ -254,13 +254,13 @@ gemm_status_t run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, c
   int dev = 0;
   if (caller_ws) {
     // Checks on the caller's workspace come before any HIP call.
-    const Plan probe = make_plan(M, N, K, A, lda, B, ldb, C, ldc, kDefaultCUs);
+    const Plan probe = make_plan(M, N, K, A, lda, B, ldb, C, ldc, kDefaultCUs, dt);
     if (probe.workspace > 0 && (ws == nullptr || ws_bytes < probe.workspace ||
                                 ((uintptr_t)ws & 255)))
       return GEMM_ERR_WORKSPACE;
   }
   if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
-  const Plan plan = make_plan(M, N, K, A, lda, B, ldb, C, ldc, device_cus(dev));
+  const Plan plan = make_plan(M, N, K, A, lda, B, ldb, C, ldc, device_cus(dev), dt);
   GemmParams p{};
   p.A = (const uint16_t*)A;
   p.B = (const uint16_t*)B;
@@ -274,7 +274,7 @@ gemm_status_t run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, c
   p.c_vec4 = plan.c_vec4 ? 1 : 0;
   p.s = plan.s;
   if (plan.kid == KID_GENERAL) {
-    return launch_general(p, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+    return launch_general(dt, p, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
   }
   if (plan.workspace > 0) {
     void* w = nullptr;
@@ -288,7 +288,8 @@ gemm_status_t run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, c
     }
     p.partials = (f32x4_storage*)w;
   }
-  return launch_tiled(plan.kid, p, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+  if (!tiled_has(plan.kid, dt)) return GEMM_ERR_NOT_SUPPORTED;
+  return launch_tiled(plan.kid, dt, p, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
 }  // namespace
@@ -297,7 +298,12 @@ extern "C" {
 
 gemm_status_t gemm_f16_f32_abt(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                                const void* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
-  return run(M, N, K, A, lda, B, ldb, C, ldc, false, nullptr, 0, stream);
+  return run(DT_F16, M, N, K, A, lda, B, ldb, C, ldc, false, nullptr, 0, stream);
+}
+
+gemm_status_t gemm_bf16_f32_abt(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                const void* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+  return run(DT_BF16, M, N, K, A, lda, B, ldb, C, ldc, false, nullptr, 0, stream);
 }
 
 size_t gemm_f16_f32_abt_workspace_size(int64_t M, int64_t N, int64_t K) {
@@ -314,7 +320,18 @@ size_t gemm_f16_f32_abt_workspace_size(int64_t M, int64_t N, int64_t K) {
 gemm_status_t gemm_f16_f32_abt_ws(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                                   const void* B, int64_t ldb, float* C, int64_t ldc,
                                   void* workspace, size_t workspace_bytes, void* stream) {
-  return run(M, N, K, A, lda, B, ldb, C, ldc, true, workspace, workspace_bytes, stream);
+  return run(DT_F16, M, N, K, A, lda, B, ldb, C, ldc, true, workspace, workspace_bytes, stream);
+}
+
+size_t gemm_bf16_f32_abt_workspace_size(int64_t M, int64_t N, int64_t K) {
+  // The plan rule does not depend on the element type.
+  return gemm_f16_f32_abt_workspace_size(M, N, K);
+}
+
+gemm_status_t gemm_bf16_f32_abt_ws(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                   const void* B, int64_t ldb, float* C, int64_t ldc,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return run(DT_BF16, M, N, K, A, lda, B, ldb, C, ldc, true, workspace, workspace_bytes, stream);
 }
 
 const char* gemm_status_string(gemm_status_t s) {

@@ -54,6 +54,13 @@ namespace g16 {
   X(33, KID_64x64x64_S8_W4, 64, 64, 64, 8, 2, 2, 32, 0, 0)             \
   X(34, KID_128x128x64_S4_W4_M16_RS, 128, 128, 64, 4, 2, 2, 16, 1, 0)
 
+// Kernel ids also built for bfloat16 operands (the shape rule's picks, and
+// the other ping-pong depths).
+#define G16_BF16_KERNELS(X) X(16) X(18) X(25) X(26) X(27)
+
+// Operand element types.
+enum DType : int32_t { DT_F16 = 0, DT_BF16 = 1 };
+
 #define G16_KID_ENUM(id, name, ...) name = id,
 enum KernelId : int32_t {
   G16_TILED_KERNELS(G16_KID_ENUM)
@@ -75,7 +82,7 @@ const KernelInfo* kernel_info(int32_t kid);
 typedef float f32x4_storage __attribute__((ext_vector_type(4)));
 
 struct GemmParams {
-  const uint16_t* A;
+  const uint16_t* A;  // binary16 or bfloat16 bit patterns
   const uint16_t* B;
   float* C;
   f32x4_storage* partials;  // [tiles][s.slots] partial tiles (split-K / stream-K only)
@@ -85,12 +92,16 @@ struct GemmParams {
   Sched s;
 };
 
-// Launches the tiled kernel `kid` with p.s.grid workgroups on `stream`, and
-// for split-K / stream-K schedules the reduce pass after it.
-hipError_t launch_tiled(int32_t kid, const GemmParams& p, hipStream_t stream);
+// Launches the tiled kernel `kid` for operand type `dt` with p.s.grid
+// workgroups on `stream`, and for split-K / stream-K schedules the reduce
+// pass after it.
+hipError_t launch_tiled(int32_t kid, int32_t dt, const GemmParams& p, hipStream_t stream);
+
+// True when tiled kernel `kid` is built for operand type `dt`.
+bool tiled_has(int32_t kid, int32_t dt);
 
 // Launches the general kernel over ceil(M/64) x ceil(N/64) workgroups.
-hipError_t launch_general(const GemmParams& p, hipStream_t stream);
+hipError_t launch_general(int32_t dt, const GemmParams& p, hipStream_t stream);
 
 // Workgroups of kernel `kid` that fit on one CU at once (0 on error).
 int32_t tiled_occupancy(int32_t kid);

@@ -36,6 +36,7 @@
 namespace g16 {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -55,28 +56,27 @@ constexpr int kReduceThreads = 256;
 // streaming stores alone.
 constexpr int kStoreNtSc1 = 2 | 16;
 
-// The two fp16 MFMA shapes with fp32 accumulation on gfx950. Both take 8
-// halves of each operand per lane; the B tile is the first operand and the A
-// tile the second (SwapAB), so a block's accumulators run along N.
+// The two MFMA shapes with fp32 accumulation on gfx950, for binary16 (DT_F16)
+// or bfloat16 (DT_BF16) operands. Both take 8 elements of each operand per
+// lane; the B tile is the first operand and the A tile the second (SwapAB),
+// so a block's accumulators run along N.
 //   32x32x16: operand lane l holds row l % 32, k = 8 (l / 32) .. +7 of the
 //     k-step; accumulator register 4g + q of lane l is row (m) l % 32,
 //     column (n) 8g + 4 (l / 32) + q of the block.
 //   16x16x32: operand lane l holds row l % 16, k = 8 (l / 16) .. +7;
 //     accumulator register q of lane l is row l % 16, column 4 (l / 16) + q.
-// On random data the 16x16x32 form reaches a higher sustained clock under
-// the board's power limit, for the same work.
+// The operand layouts do not depend on the element type. On random data the
+// 16x16x32 form reaches a higher sustained clock under the board's power
+// limit, for the same work.
 template <int MI>
-struct Mma;
+struct MmaShape;
 
 template <>
-struct Mma<32> {
+struct MmaShape<32> {
   static constexpr int DIM = 32;    // rows (and columns) of an accumulator block
   static constexpr int KW = 16;     // k per instruction
   static constexpr int GROUPS = 4;  // runs of 4 consecutive columns per lane
   typedef f32x16 acc_t;
-  static __device__ __forceinline__ acc_t mma(half8 b, half8 a, acc_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0);
-  }
   static __device__ __forceinline__ int frag_row(int lane) { return lane & 31; }
   static __device__ __forceinline__ int frag_chunk(int ks, int lane) { return 2 * ks + (lane >> 5); }
   static __device__ __forceinline__ int acc_m(int lane) { return lane & 31; }
@@ -84,18 +84,54 @@ struct Mma<32> {
 };
 
 template <>
-struct Mma<16> {
+struct MmaShape<16> {
   static constexpr int DIM = 16;
   static constexpr int KW = 32;
   static constexpr int GROUPS = 1;
   typedef f32x4 acc_t;
-  static __device__ __forceinline__ acc_t mma(half8 b, half8 a, acc_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, c, 0, 0, 0);
-  }
   static __device__ __forceinline__ int frag_row(int lane) { return lane & 15; }
   static __device__ __forceinline__ int frag_chunk(int ks, int lane) { return 4 * ks + (lane >> 4); }
   static __device__ __forceinline__ int acc_m(int lane) { return lane & 15; }
   static __device__ __forceinline__ int acc_n(int, int lane) { return 4 * (lane >> 4); }
+};
+
+template <int MI, int DT>
+struct Mma;
+
+template <>
+struct Mma<32, DT_F16> : MmaShape<32> {
+  typedef half8 frag_t;
+  typedef _Float16 elem_t;
+  static __device__ __forceinline__ acc_t mma(frag_t b, frag_t a, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mma<16, DT_F16> : MmaShape<16> {
+  typedef half8 frag_t;
+  typedef _Float16 elem_t;
+  static __device__ __forceinline__ acc_t mma(frag_t b, frag_t a, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mma<32, DT_BF16> : MmaShape<32> {
+  typedef bf16x8 frag_t;
+  typedef __bf16 elem_t;
+  static __device__ __forceinline__ acc_t mma(frag_t b, frag_t a, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mma<16, DT_BF16> : MmaShape<16> {
+  typedef bf16x8 frag_t;
+  typedef __bf16 elem_t;
+  static __device__ __forceinline__ acc_t mma(frag_t b, frag_t a, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a, c, 0, 0, 0);
+  }
 };
 
 // RS_: when the fragment reads of the next k-step are issued. 0: spread
@@ -103,15 +139,17 @@ struct Mma<16> {
 // the fragment it replaces, so the current and next fragments barely overlap
 // in registers (for register-bound variants).
 // PP_: 1 selects the ping-pong main loop (gemm_pingpong_kernel, 8 waves).
+// DT_: operand element type (DT_F16 or DT_BF16).
 template <int BM_, int BN_, int BK_, int STAGES_, int WGM_, int WGN_, int MI_ = 32, int RS_ = 0,
-          int PP_ = 0>
+          int PP_ = 0, int DT_ = DT_F16>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
   static constexpr int WGM = WGM_, WGN = WGN_;
   static constexpr int MI = MI_;
   static constexpr int RS = RS_;
   static constexpr int PP = PP_;
-  using M = Mma<MI>;
+  static constexpr int DT = DT_;
+  using M = Mma<MI, DT>;
   using acc_t = typename M::acc_t;
   static constexpr int WAVES = WGM * WGN;
   static constexpr int THREADS = WAVES * 64;
@@ -215,8 +253,8 @@ __device__ __forceinline__ void phase_barrier() {
 
 template <class C>
 struct Frags {
-  half8 a[C::FM];
-  half8 b[C::FN];
+  typename C::M::frag_t a[C::FM];
+  typename C::M::frag_t b[C::FN];
 };
 
 // Per-lane LDS byte offset (relative to a stage) of the fragment of k-step
@@ -232,11 +270,11 @@ __device__ __forceinline__ void read_frags(const char* stage, int ks, int wm, in
                                            Frags<C>& f) {
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
-    f.a[i] = *reinterpret_cast<const half8*>(
+    f.a[i] = *reinterpret_cast<const typename C::M::frag_t*>(
         stage + frag_off<C>(wm * C::WM + i * C::M::DIM, ks, lane));
 #pragma unroll
   for (int j = 0; j < C::FN; ++j)
-    f.b[j] = *reinterpret_cast<const half8*>(
+    f.b[j] = *reinterpret_cast<const typename C::M::frag_t*>(
         stage + C::A_BYTES + frag_off<C>(wn * C::WN + j * C::M::DIM, ks, lane));
 }
 
@@ -355,10 +393,10 @@ template <class C, int R>
 __device__ __forceinline__ void read_one(Frags<C>& nxt, const char* rstage, int rks, int wm,
                                          int wn, int lane) {
   if constexpr (R < C::FM) {
-    nxt.a[R] = *reinterpret_cast<const half8*>(
+    nxt.a[R] = *reinterpret_cast<const typename C::M::frag_t*>(
         rstage + frag_off<C>(wm * C::WM + R * C::M::DIM, rks, lane));
   } else {
-    nxt.b[R - C::FM] = *reinterpret_cast<const half8*>(
+    nxt.b[R - C::FM] = *reinterpret_cast<const typename C::M::frag_t*>(
         rstage + C::A_BYTES + frag_off<C>(wn * C::WN + (R - C::FM) * C::M::DIM, rks, lane));
   }
 }
@@ -918,7 +956,10 @@ __global__ __launch_bounds__(kReduceThreads) void gemm_reduce_kernel(GemmParams 
 // operands go straight from global memory into MFMA registers, element by
 // element with bounds checks. Slow; taken only when the tiled kernels'
 // alignment rules do not hold.
+template <int DT>
 __global__ __launch_bounds__(256) void gemm_general_kernel(GemmParams p, int32_t tiles_n) {
+  using M = Mma<32, DT>;
+  typedef typename M::elem_t elem_t;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int tm = blockIdx.x / tiles_n;
@@ -934,15 +975,15 @@ __global__ __launch_bounds__(256) void gemm_general_kernel(GemmParams p, int32_t
   const uint16_t* brow = p.B + (int64_t)(b_ok ? br : 0) * p.ldb;
   f32x16 acc = {};
   for (int k0 = 0; k0 < p.K; k0 += 16) {
-    half8 a, b;
+    typename M::frag_t a, b;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int k = k0 + kk + e;
       const bool kin = k < p.K;
-      a[e] = (a_ok && kin) ? __builtin_bit_cast(_Float16, arow[k]) : (_Float16)0;
-      b[e] = (b_ok && kin) ? __builtin_bit_cast(_Float16, brow[k]) : (_Float16)0;
+      a[e] = __builtin_bit_cast(elem_t, (a_ok && kin) ? arow[k] : (uint16_t)0);
+      b[e] = __builtin_bit_cast(elem_t, (b_ok && kin) ? brow[k] : (uint16_t)0);
     }
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, acc, 0, 0, 0);
+    acc = M::mma(b, a, acc);
   }
   const int m = m0 + (lane & 31);
   if (m < p.M) {
@@ -958,6 +999,10 @@ __global__ __launch_bounds__(256) void gemm_general_kernel(GemmParams p, int32_t
   using K##id = Cfg<bm, bn, bk, st, wgm, wgn, mi, rs, pp>;
 G16_TILED_KERNELS(G16_CFG)
 #undef G16_CFG
+
+// The same configuration with bfloat16 operands.
+template <class C>
+using Bf16Of = Cfg<C::BM, C::BN, C::BK, C::STAGES, C::WGM, C::WGN, C::MI, C::RS, C::PP, DT_BF16>;
 
 template <class C>
 constexpr KernelInfo info_of(const char* name) {
@@ -1025,7 +1070,16 @@ const KernelInfo* kernel_info(int32_t kid) {
   return &kInfos[kid];
 }
 
-hipError_t launch_tiled(int32_t kid, const GemmParams& p, hipStream_t stream) {
+hipError_t launch_tiled(int32_t kid, int32_t dt, const GemmParams& p, hipStream_t stream) {
+  if (dt == DT_BF16) {
+#define G16_LAUNCH_BF16(id) \
+  case id: return launch_cfg<Bf16Of<K##id>>(p, stream);
+    switch (kid) {
+      G16_BF16_KERNELS(G16_LAUNCH_BF16)
+      default: return hipErrorInvalidValue;
+    }
+#undef G16_LAUNCH_BF16
+  }
 #define G16_LAUNCH(id, name, ...) \
   case name: return launch_cfg<K##id>(p, stream);
   switch (kid) {
@@ -1033,6 +1087,16 @@ hipError_t launch_tiled(int32_t kid, const GemmParams& p, hipStream_t stream) {
     default: return hipErrorInvalidValue;
   }
 #undef G16_LAUNCH
+}
+
+bool tiled_has(int32_t kid, int32_t dt) {
+  if (kid < 0 || kid >= KID_COUNT) return false;
+  if (dt == DT_F16) return true;
+  if (dt != DT_BF16) return false;
+#define G16_HAS_BF16(id) if (kid == id) return true;
+  G16_BF16_KERNELS(G16_HAS_BF16)
+#undef G16_HAS_BF16
+  return false;
 }
 
 int32_t tiled_occupancy(int32_t kid) {
@@ -1045,14 +1109,18 @@ int32_t tiled_occupancy(int32_t kid) {
 #undef G16_OCC
 }
 
-hipError_t launch_general(const GemmParams& p, hipStream_t stream) {
+hipError_t launch_general(int32_t dt, const GemmParams& p, hipStream_t stream) {
   const int64_t tiles_m = (p.M + 63) / 64;
   const int64_t tiles_n = (p.N + 63) / 64;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm_general_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, p,
-                     (int32_t)tiles_n);
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL(gemm_general_kernel<DT_BF16>, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                       p, (int32_t)tiles_n);
+  else
+    hipLaunchKernelGGL(gemm_general_kernel<DT_F16>, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                       p, (int32_t)tiles_n);
   return hipGetLastError();
 }
 

@@ -24,7 +24,8 @@ STATUS_NAMES = {
 EXPORTS = (
     "gemm_f16_f32_abt", "gemm_f16_f32_abt_workspace_size", "gemm_f16_f32_abt_ws",
     "gemm_status_string", "gemm_f16_f32_abt_describe", "gemm_f16_release_workspaces",
-    "gemm_f16_schedule_dump",
+    "gemm_f16_schedule_dump", "gemm_bf16_f32_abt", "gemm_bf16_f32_abt_workspace_size",
+    "gemm_bf16_f32_abt_ws",
 )
 
 _lib = None
@@ -53,6 +54,12 @@ def load(path: str = LIBRARY):
     lib.gemm_f16_f32_abt_workspace_size.restype = sz
     lib.gemm_f16_f32_abt_ws.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, sz, p]
     lib.gemm_f16_f32_abt_ws.restype = st
+    lib.gemm_bf16_f32_abt.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
+    lib.gemm_bf16_f32_abt.restype = st
+    lib.gemm_bf16_f32_abt_workspace_size.argtypes = [i64, i64, i64]
+    lib.gemm_bf16_f32_abt_workspace_size.restype = sz
+    lib.gemm_bf16_f32_abt_ws.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, sz, p]
+    lib.gemm_bf16_f32_abt_ws.restype = st
     lib.gemm_status_string.argtypes = [st]
     lib.gemm_status_string.restype = ctypes.c_char_p
     lib.gemm_f16_f32_abt_describe.argtypes = [i64, i64, i64, ctypes.c_char_p, sz]
@@ -89,6 +96,21 @@ def gemm_f16_f32_abt_workspace_size(M, N, K) -> int:
     return load().gemm_f16_f32_abt_workspace_size(M, N, K)
 
 
+def gemm_bf16_f32_abt(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    """Raw call with bfloat16 operands; returns the status code (does not raise)."""
+    return load().gemm_bf16_f32_abt(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_bf16_f32_abt_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes,
+                         stream=0) -> int:
+    return load().gemm_bf16_f32_abt_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace,
+                                       workspace_bytes, stream)
+
+
+def gemm_bf16_f32_abt_workspace_size(M, N, K) -> int:
+    return load().gemm_bf16_f32_abt_workspace_size(M, N, K)
+
+
 def gemm_status_string(status: int) -> str:
     return load().gemm_status_string(status).decode()
 
@@ -122,13 +144,15 @@ def gemm_f16_schedule_dump(M, N, K, grid=0):
 # --- torch convenience -----------------------------------------------------
 
 def gemm_abt(A, B, C=None, stream=None, workspace=None):
-    """C = A @ B^T for torch tensors: A (M, K) and B (N, K) float16, C (M, N)
-    float32, all on one GPU with unit stride along the last dimension.
-    Returns C. Enqueued on ``stream`` (default: torch's current stream)."""
+    """C = A @ B^T for torch tensors: A (M, K) and B (N, K) both float16 or
+    both bfloat16, C (M, N) float32, all on one GPU with unit stride along the
+    last dimension. Returns C. Enqueued on ``stream`` (default: torch's
+    current stream)."""
     import torch
 
-    if A.dtype != torch.float16 or B.dtype != torch.float16:
-        raise TypeError("A and B must be float16")
+    if A.dtype != B.dtype or A.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("A and B must be both float16 or both bfloat16")
+    bf16 = A.dtype == torch.bfloat16
     if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[1]:
         raise ValueError("A must be (M, K) and B (N, K)")
     M, K = A.shape
@@ -150,11 +174,11 @@ def gemm_abt(A, B, C=None, stream=None, workspace=None):
     s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     with torch.cuda.device(A.device):
         if workspace is None:
-            st = gemm_f16_f32_abt(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(),
-                                  ldc, s)
+            fn = gemm_bf16_f32_abt if bf16 else gemm_f16_f32_abt
+            st = fn(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, s)
         else:
-            st = gemm_f16_f32_abt_ws(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
-                                     C.data_ptr(), ldc, workspace.data_ptr(),
-                                     workspace.numel() * workspace.element_size(), s)
+            fn = gemm_bf16_f32_abt_ws if bf16 else gemm_f16_f32_abt_ws
+            st = fn(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,
+                    workspace.data_ptr(), workspace.numel() * workspace.element_size(), s)
     _check(st)
     return C

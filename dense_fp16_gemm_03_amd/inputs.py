@@ -17,6 +17,11 @@ Structured operands (identity, a permutation-like pattern, all-ones and a
 k-block-weighted ones pattern) give closed-form products for the pins.
 
 Standard seeds: A = 1, B = 2 for ``uniform``; A = 3, B = 4 for ``integer``.
+
+bfloat16 operands are numpy ``uint16`` arrays of bfloat16 bit patterns (numpy
+has no bfloat16 type): the same draws, rounded binary64 -> binary32 -> bfloat16,
+each step to nearest-even (``to_bf16_bits``). Integers up to 256 in magnitude
+and the structured patterns below are exact in bfloat16.
 """
 from __future__ import annotations
 
@@ -105,9 +110,53 @@ def kblock_weights(rows: int, cols: int, block: int) -> np.ndarray:
     return np.broadcast_to(w.astype(np.float16), (rows, cols)).copy()
 
 
-def workload_operands(shape, kind: str = "uniform"):
-    """(A, B) for an (M, N, K) shape with the standard seeds of ``kind``."""
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of finite values: round to binary32, then
+    keep the upper 16 bits rounded to nearest-even on the lower 16."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = b + np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))
+    return (b >> np.uint64(16)).astype(np.uint16)
+
+
+def uniform_bf16(rows: int, cols: int, seed: int) -> np.ndarray:
+    """rows x cols bfloat16 bits, i.i.d. uniform on [-1, 1] (the ``uniform`` draw)."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((rows, cols), dtype=np.uint16)
+    step = max(1, (1 << 24) // max(cols, 1))
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
+        out[r0:r1] = to_bf16_bits(rng.uniform(-1.0, 1.0, size=(r1 - r0, cols)))
+    return out
+
+
+def integer_bf16(rows: int, cols: int, seed: int, lo: int = -2, hi: int = 2) -> np.ndarray:
+    """rows x cols bfloat16 bits holding i.i.d. integers uniform on {lo..hi}."""
+    rng = np.random.default_rng(seed)
+    return to_bf16_bits(rng.integers(lo, hi + 1, size=(rows, cols)))
+
+
+def perm_pattern_bf16(rows: int, cols: int) -> np.ndarray:
+    """P[j][k] = ((37 j + 11 k) mod 256) - 128 as bfloat16 bits (exact)."""
+    j = np.arange(rows, dtype=np.int64)[:, None]
+    k = np.arange(cols, dtype=np.int64)[None, :]
+    return to_bf16_bits(((37 * j + 11 * k) % 256) - 128)
+
+
+def workload_operands(shape, kind: str = "uniform", dtype: str = "f16"):
+    """(A, B) for an (M, N, K) shape with the standard seeds of ``kind``;
+    dtype "bf16" gives bfloat16 bit arrays (uint16) of the same draws."""
     M, N, K = shape
+    if dtype == "bf16":
+        if kind == "uniform":
+            return uniform_bf16(M, K, SEED_A_UNIFORM), uniform_bf16(N, K, SEED_B_UNIFORM)
+        if kind == "integer":
+            return integer_bf16(M, K, SEED_A_INTEGER), integer_bf16(N, K, SEED_B_INTEGER)
+        if kind == "hash_int":
+            return (to_bf16_bits(hash_int(M, K, 1).astype(np.float32)),
+                    to_bf16_bits(hash_int(N, K, 2).astype(np.float32)))
+        raise ValueError(f"unknown input kind {kind!r}")
+    if dtype != "f16":
+        raise ValueError(f"unknown dtype {dtype!r}")
     if kind == "uniform":
         return uniform(M, K, SEED_A_UNIFORM), uniform(N, K, SEED_B_UNIFORM)
     if kind == "integer":

@@ -70,6 +70,30 @@ gemm_status_t gemm_f16_f32_abt_ws(int64_t M, int64_t N, int64_t K,
                                   float* C, int64_t ldc,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* bfloat16 inputs: as gemm_f16_f32_abt, with A and B holding bfloat16 bit
+ * patterns (the upper 16 bits of an IEEE binary32: 1 sign bit, 8 exponent
+ * bits with bias 127, 7 fraction bits) instead of binary16. Same layouts,
+ * semantics, alignment rules, workspace and error behaviour; accumulation
+ * and output stay binary32. bfloat16 is the 16-bit type the cuBLASDx "BLAS
+ * Performance Guide" handles beside half (section "Build Card", on the half
+ * and bfloat16 conversions its headers need); the path is otherwise the
+ * fp16 one, on the bf16 forms of the same MFMA instructions. */
+gemm_status_t gemm_bf16_f32_abt(int64_t M, int64_t N, int64_t K,
+                                const void* A, int64_t lda,
+                                const void* B, int64_t ldb,
+                                float* C, int64_t ldc, void* stream);
+
+/* Bytes of workspace gemm_bf16_f32_abt_ws needs for this shape (0 if none);
+ * the same as gemm_f16_f32_abt_workspace_size. */
+size_t gemm_bf16_f32_abt_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* gemm_bf16_f32_abt with a caller-owned workspace, as gemm_f16_f32_abt_ws. */
+gemm_status_t gemm_bf16_f32_abt_ws(int64_t M, int64_t N, int64_t K,
+                                   const void* A, int64_t lda,
+                                   const void* B, int64_t ldb,
+                                   float* C, int64_t ldc,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* gemm_status_string(gemm_status_t s);
 

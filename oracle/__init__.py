@@ -1,4 +1,4 @@
-"""Reference for C = A * B^T on binary16 inputs, summed in binary64.
+"""Reference for C = A * B^T on binary16 (or bfloat16) inputs, summed in binary64.
 
 TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
 baseline use it; the product library never does, and nothing here imports the
@@ -15,7 +15,10 @@ Pins (tests/test_oracle.py): exhaustive binary16 decode against numpy; brute
 force in exact rational arithmetic on tiny inputs; identity, permutation and
 all-ones closed forms; the transpose invariant; numpy binary64 matmul; the
 absolute-sum identity S(A, B) = C(|A|, |B|); planted-mistake variants of the
-C source that each pin must reject.
+C source that each pin must reject. The bfloat16 entry points (``*_bf16``)
+take uint16 arrays of bfloat16 bit patterns and have pins of their own
+(exhaustive decode against numpy's binary32 reading of the same bits, known
+values, brute force, closed forms, numpy matmul).
 """
 from __future__ import annotations
 
@@ -49,6 +52,12 @@ def _bind(lib):
     lib.oracle_gemm_abt.restype = ctypes.c_int
     lib.oracle_gemm_abt_elems.argtypes = [i64, p, p, i64, p, i64, p, i64, p, p, ctypes.c_int]
     lib.oracle_gemm_abt_elems.restype = ctypes.c_int
+    lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_double.restype = ctypes.c_double
+    lib.oracle_gemm_abt_bf16.argtypes = lib.oracle_gemm_abt.argtypes
+    lib.oracle_gemm_abt_bf16.restype = ctypes.c_int
+    lib.oracle_gemm_abt_elems_bf16.argtypes = lib.oracle_gemm_abt_elems.argtypes
+    lib.oracle_gemm_abt_elems_bf16.restype = ctypes.c_int
     return lib
 
 
@@ -79,6 +88,14 @@ def _as_f16_rows(x: np.ndarray, name: str) -> np.ndarray:
     return x
 
 
+def _as_bf16_rows(x: np.ndarray, name: str) -> np.ndarray:
+    if x.dtype != np.uint16 or x.ndim != 2:
+        raise TypeError(f"{name} must be a 2-D uint16 array of bfloat16 bit patterns")
+    if x.size and x.shape[1] > 1 and x.strides[1] != 2:
+        raise ValueError(f"{name} rows must be contiguous")
+    return x
+
+
 def _ld(x: np.ndarray) -> int:
     """Row stride in elements (any value >= K is fine for one-row or empty arrays)."""
     if x.shape[0] <= 1 or x.size == 0:
@@ -91,20 +108,36 @@ def half_to_double(bits: int, lib=None) -> float:
     return (lib or load()).oracle_half_to_double(bits)
 
 
+def bf16_to_double(bits: int, lib=None) -> float:
+    """Decode one bfloat16 bit pattern (0..65535)."""
+    return (lib or load()).oracle_bf16_to_double(bits)
+
+
 def gemm_abt(A: np.ndarray, B: np.ndarray, threads: int | None = None, lib=None):
     """Return (C, S): C = A B^T and S = sum_k |a_ik b_jk|, both float64 M x N."""
     lib = lib or load()
     A = _as_f16_rows(A, "A")
     B = _as_f16_rows(B, "B")
+    return _full(lib.oracle_gemm_abt, A, B, threads)
+
+
+def gemm_abt_bf16(A: np.ndarray, B: np.ndarray, threads: int | None = None, lib=None):
+    """gemm_abt for bfloat16 operands given as uint16 bit-pattern arrays."""
+    lib = lib or load()
+    A = _as_bf16_rows(A, "A")
+    B = _as_bf16_rows(B, "B")
+    return _full(lib.oracle_gemm_abt_bf16, A, B, threads)
+
+
+def _full(fn, A, B, threads):
     M, K = A.shape
     N, Kb = B.shape
     if Kb != K:
         raise ValueError("A and B must have the same number of columns K")
     C = np.empty((M, N), dtype=np.float64)
     S = np.empty((M, N), dtype=np.float64)
-    r = lib.oracle_gemm_abt(M, N, K, A.ctypes.data, _ld(A), B.ctypes.data,
-                            _ld(B), C.ctypes.data, N, S.ctypes.data, N,
-                            threads or default_threads())
+    r = fn(M, N, K, A.ctypes.data, _ld(A), B.ctypes.data, _ld(B), C.ctypes.data, N,
+           S.ctypes.data, N, threads or default_threads())
     if r < 0:
         raise ValueError("oracle rejected the arguments")
     return C, S
@@ -116,6 +149,19 @@ def gemm_abt_elems(A: np.ndarray, B: np.ndarray, rows, cols, threads: int | None
     lib = lib or load()
     A = _as_f16_rows(A, "A")
     B = _as_f16_rows(B, "B")
+    return _elems(lib.oracle_gemm_abt_elems, A, B, rows, cols, threads)
+
+
+def gemm_abt_elems_bf16(A: np.ndarray, B: np.ndarray, rows, cols, threads: int | None = None,
+                        lib=None):
+    """gemm_abt_elems for bfloat16 operands given as uint16 bit-pattern arrays."""
+    lib = lib or load()
+    A = _as_bf16_rows(A, "A")
+    B = _as_bf16_rows(B, "B")
+    return _elems(lib.oracle_gemm_abt_elems_bf16, A, B, rows, cols, threads)
+
+
+def _elems(fn, A, B, rows, cols, threads):
     K = A.shape[1]
     if B.shape[1] != K:
         raise ValueError("A and B must have the same number of columns K")
@@ -128,10 +174,8 @@ def gemm_abt_elems(A: np.ndarray, B: np.ndarray, rows, cols, threads: int | None
         raise IndexError("element index out of range")
     C = np.empty(rows.size, dtype=np.float64)
     S = np.empty(rows.size, dtype=np.float64)
-    r = lib.oracle_gemm_abt_elems(rows.size, rows.ctypes.data, cols.ctypes.data, K,
-                                  A.ctypes.data, _ld(A), B.ctypes.data,
-                                  _ld(B), C.ctypes.data, S.ctypes.data,
-                                  threads or default_threads())
+    r = fn(rows.size, rows.ctypes.data, cols.ctypes.data, K, A.ctypes.data, _ld(A),
+           B.ctypes.data, _ld(B), C.ctypes.data, S.ctypes.data, threads or default_threads())
     if r < 0:
         raise ValueError("oracle rejected the arguments")
     return C, S

@@ -199,6 +199,123 @@ def pin_elems(lib) -> list:
     return [] if ok else ["elems != full"]
 
 
+# --- bfloat16 entry points ---------------------------------------------------
+
+def _bf16_values(bits: np.ndarray) -> np.ndarray:
+    """numpy's own binary32 reading of bfloat16 bits (the upper half of a binary32)."""
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns
+        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def pin_bf16_exhaustive(lib) -> list:
+    """All 65536 bfloat16 patterns decode as numpy reads the same bits as binary32."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = _bf16_values(bits)
+    got = np.array([lib.oracle_bf16_to_double(int(b)) for b in bits])
+    bad = []
+    nan_ref, nan_got = np.isnan(ref), np.isnan(got)
+    if not np.array_equal(nan_ref, nan_got):
+        bad.append(f"NaN classification differs at {np.flatnonzero(nan_ref != nan_got)[:5]}")
+    fin = ~nan_ref & ~nan_got
+    diff = fin & ((got != ref) | (np.signbit(got) != np.signbit(ref)))
+    if diff.any():
+        i = np.flatnonzero(diff)[:5]
+        bad.append(f"bf16 decode differs at {[hex(int(b)) for b in i]}: {got[i]} vs {ref[i]}")
+    return bad
+
+
+# bfloat16 values fixed by the format (1 sign, 8 exponent bits with bias 127, 7 fraction bits).
+BF16_KNOWN = {
+    0x0000: 0.0, 0x8000: -0.0, 0x3F80: 1.0, 0xBF80: -1.0, 0x4000: 2.0, 0x3F00: 0.5,
+    0x3EAB: 0.333984375, 0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127, 0x0080: 2.0 ** -126,
+    0x0001: 2.0 ** -133, 0x007F: 127 * 2.0 ** -133, 0x4300: 128.0, 0x4380: 256.0,
+    0x7F80: float("inf"), 0xFF80: float("-inf"),
+}
+
+
+def pin_bf16_known(lib) -> list:
+    bad = []
+    for h, v in BF16_KNOWN.items():
+        g = lib.oracle_bf16_to_double(h)
+        if g != v or np.signbit(g) != np.signbit(v):
+            bad.append(f"bf16 {h:#06x} -> {g}, expected {v}")
+    for h in (0x7F81, 0x7FC0, 0xFFFF):
+        if not np.isnan(lib.oracle_bf16_to_double(h)):
+            bad.append(f"bf16 {h:#06x} should be NaN")
+    return bad
+
+
+def pin_bf16_brute_integer(lib) -> list:
+    """Tiny shapes, integer bfloat16 entries: exact Python-integer sums."""
+    rng = np.random.default_rng(13)
+    for M, N, K in ((1, 1, 1), (2, 3, 5), (5, 2, 17), (3, 3, 33), (8, 5, 9)):
+        ai = rng.integers(-3, 4, size=(M, K))
+        bi = rng.integers(-3, 4, size=(N, K))
+        C, S = oracle.gemm_abt_bf16(inputs.to_bf16_bits(ai), inputs.to_bf16_bits(bi),
+                                    threads=2, lib=lib)
+        for i in range(M):
+            for j in range(N):
+                c = sum(int(ai[i, k]) * int(bi[j, k]) for k in range(K))
+                s = sum(abs(int(ai[i, k]) * int(bi[j, k])) for k in range(K))
+                if C[i, j] != c or S[i, j] != s:
+                    return [f"bf16 {M}x{N}x{K} at ({i},{j}): C {C[i, j]} vs {c}, S {S[i, j]} vs {s}"]
+    return []
+
+
+def pin_bf16_closed_forms(lib) -> list:
+    """Identity, a non-symmetric bfloat16-exact pattern, all-ones and k-block weights."""
+    bad = []
+    K = 48
+    I = inputs.to_bf16_bits(np.eye(K))
+    X = inputs.uniform_bf16(40, K, 33)
+    C, _ = oracle.gemm_abt_bf16(I, X, lib=lib)
+    if not np.array_equal(C, _bf16_values(X).T):
+        bad.append("bf16 A = I: C != B^T")
+    C, _ = oracle.gemm_abt_bf16(X, I, lib=lib)
+    if not np.array_equal(C, _bf16_values(X)):
+        bad.append("bf16 B = I: C != A")
+    P = inputs.perm_pattern_bf16(50, 64)
+    C, _ = oracle.gemm_abt_bf16(inputs.to_bf16_bits(np.eye(64)), P, lib=lib)
+    if not np.array_equal(C, _bf16_values(P).T):
+        bad.append("bf16 perm pattern: C != B^T")
+    for K in (1, 7, 129):
+        one = inputs.to_bf16_bits(np.ones((3, K)))
+        C, S = oracle.gemm_abt_bf16(one, one[:2], lib=lib)
+        if not (np.all(C == K) and np.all(S == K)):
+            bad.append(f"bf16 ones K={K}: {C.ravel()[:3]}")
+    K, blk = 1000, 64
+    w = inputs.to_bf16_bits(1 + ((np.arange(K) // blk) % 7))[None, :].repeat(3, axis=0)
+    C, _ = oracle.gemm_abt_bf16(inputs.to_bf16_bits(np.ones((2, K))), w, lib=lib)
+    expect = sum((1 + (b % 7)) * min(blk, K - b * blk) for b in range((K + blk - 1) // blk))
+    if not np.all(C == expect):
+        bad.append(f"bf16 k-block weights: {C.ravel()[:3]} vs {expect}")
+    return bad
+
+
+def pin_bf16_numpy_and_transpose(lib) -> list:
+    """numpy binary64 matmul of numpy-decoded operands; transpose invariant; elements."""
+    bad = []
+    M = N = K = 128
+    A, B = inputs.workload_operands((M, N, K), "integer", "bf16")
+    C, _ = oracle.gemm_abt_bf16(A, B, lib=lib)
+    if not np.array_equal(C, _bf16_values(A) @ _bf16_values(B).T):
+        bad.append("bf16 integer: oracle != numpy")
+    A, B = inputs.workload_operands((M, N, K), "uniform", "bf16")
+    C, S = oracle.gemm_abt_bf16(A, B, lib=lib)
+    ref = _bf16_values(A) @ _bf16_values(B).T
+    if not np.all(np.abs(C - ref) <= 2 * K * 2.0 ** -52 * S):
+        bad.append("bf16 uniform: oracle != numpy within the binary64 bound")
+    C2, S2 = oracle.gemm_abt_bf16(B, A, lib=lib)
+    if not (np.array_equal(C, C2.T) and np.array_equal(S, S2.T)):
+        bad.append("bf16 transpose invariant broken")
+    rows, cols = np.array([0, 127, 5, 64]), np.array([127, 0, 9, 64])
+    c, s = oracle.gemm_abt_elems_bf16(A, B, rows, cols, lib=lib)
+    if not (np.array_equal(c, C[rows, cols]) and np.array_equal(s, S[rows, cols])):
+        bad.append("bf16 elems != full")
+    return bad
+
+
 ALL_PINS = [pin_half_exhaustive, pin_half_known, pin_brute_integer, pin_brute_rational,
             pin_identity, pin_perm, pin_ones, pin_transpose, pin_abs_identity, pin_numpy,
-            pin_strided, pin_elems]
+            pin_strided, pin_elems, pin_bf16_exhaustive, pin_bf16_known,
+            pin_bf16_brute_integer, pin_bf16_closed_forms, pin_bf16_numpy_and_transpose]

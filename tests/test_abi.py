@@ -62,6 +62,22 @@ A_PTR, B_PTR, C_PTR = 0x10000000, 0x20000000, 0x30000000
 ])
 def test_argument_checks(lib, args, expect):
     assert gemm.gemm_f16_f32_abt(*args, 0) == expect
+    assert gemm.gemm_bf16_f32_abt(*args, 0) == expect  # same contract for bfloat16
+
+
+def test_bf16_workspace_and_dtype_checks(lib):
+    import torch
+
+    for shape in ((2048, 2048, 16384), (1024, 1024, 65536), (8192, 8192, 8192), (7, 9, 13)):
+        assert (gemm.gemm_bf16_f32_abt_workspace_size(*shape)
+                == gemm.gemm_f16_f32_abt_workspace_size(*shape))
+    M, N, K = inputs.WORKLOADS["1024x1024x65536"]
+    assert gemm.gemm_bf16_f32_abt_ws(M, N, K, A_PTR, K, B_PTR, K, C_PTR, N, 0, 0, 0) == 5
+    with pytest.raises(TypeError):  # mixed operand types, rejected before any device call
+        gemm.gemm_abt(torch.zeros(2, 2, dtype=torch.float16),
+                      torch.zeros(2, 2, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        gemm.gemm_abt(torch.zeros(2, 2), torch.zeros(2, 2))
 
 
 def test_caller_workspace_checked_first(lib):

@@ -51,3 +51,40 @@ def test_kblock_weights():
 def test_workloads_table():
     assert inputs.WORKLOADS["8192^3"] == (8192, 8192, 8192)
     assert inputs.WORKLOADS["1024x1024x65536"] == (1024, 1024, 65536)
+
+
+def _bf16_values(bits):
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def test_to_bf16_bits_matches_torch_rounding():
+    """Round-to-nearest-even binary32 -> bfloat16, checked against torch's own
+    conversion (an independent implementation), halfway cases included."""
+    import torch
+
+    rng = np.random.default_rng(5)
+    x = rng.uniform(-4, 4, size=20000).astype(np.float32)
+    base = (np.arange(1, 2001, dtype=np.uint32) << np.uint32(16))
+    halfway = np.concatenate([(base | np.uint32(0x8000)).view(np.float32),   # ties
+                              (base | np.uint32(0x7FFF)).view(np.float32),
+                              (base | np.uint32(0x8001)).view(np.float32)])
+    for v in (x, halfway, -halfway):
+        ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(inputs.to_bf16_bits(v), ref)
+
+
+def test_bf16_generators():
+    a = inputs.uniform_bf16(300, 70, 1)
+    assert a.dtype == np.uint16 and a.shape == (300, 70)
+    assert np.array_equal(a, inputs.uniform_bf16(300, 70, 1))
+    va = _bf16_values(a)
+    assert va.min() >= -1 and va.max() <= 1
+    ref = np.random.default_rng(1).uniform(-1.0, 1.0, size=(300, 70))
+    assert np.array_equal(a, inputs.to_bf16_bits(ref))
+    i = inputs.integer_bf16(200, 64, 3)
+    assert set(np.unique(_bf16_values(i)).tolist()) == {-2.0, -1.0, 0.0, 1.0, 2.0}
+    p = inputs.perm_pattern_bf16(100, 300)
+    j, k = np.meshgrid(np.arange(100), np.arange(300), indexing="ij")
+    assert np.array_equal(_bf16_values(p).astype(np.int64), ((37 * j + 11 * k) % 256) - 128)
+    A, B = inputs.workload_operands((64, 32, 16), "hash_int", "bf16")
+    assert np.array_equal(_bf16_values(A), inputs.hash_int(64, 16, 1).astype(np.float32))

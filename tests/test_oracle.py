@@ -2,8 +2,9 @@
 
 A planted mistake in the reference's C source (compiled into a scratch
 library) must be caught by at least one pin; that shows the pins constrain
-each part of the reference: the binary16 decode, the k range, operand
-indexing, the output index and the absolute sum.
+each part of the reference: the binary16 and bfloat16 decodes, the k range,
+operand indexing, the output index, the absolute sum and the format each
+entry point decodes.
 """
 import os
 
@@ -89,6 +90,19 @@ MUTATIONS = [
     ("implicit bit missing", "(double)(1024 + frac)", "(double)(frac)"),
     ("Inf read as NaN", "frac == 0 ? INFINITY : NAN", "NAN"),
     ("k loop reads element k+1", "dec[a_row[k]] * dec[b_row[k]]", "dec[a_row[k]] * dec[b_row[k + (k + 1 < K)]]"),
+    ("bf16 exponent bias off by one", "expo - 134", "expo - 133"),
+    ("bf16 subnormal scale wrong", "ldexp((double)frac, -133)", "ldexp((double)frac, -132)"),
+    ("bf16 implicit bit missing", "(double)(128 + frac)", "(double)(frac)"),
+    ("bf16 exponent field misplaced", "(h >> 7) & 0xff", "(h >> 8) & 0xff"),
+    ("bf16 fraction field narrowed", "h & 0x7f;", "h & 0x3f;"),
+    ("bf16 operands decoded as binary16", "return fmt == 1 ? g_bf16_table : g_half_table;",
+     "return g_half_table;"),
+    ("binary16 operands decoded as bf16", "return fmt == 1 ? g_bf16_table : g_half_table;",
+     "return g_bf16_table;"),
+    ("bf16 entry point passes the binary16 format", "return gemm_full(1, M, N, K",
+     "return gemm_full(0, M, N, K"),
+    ("bf16 element entry passes the binary16 format", "return gemm_elems(1, n",
+     "return gemm_elems(0, n"),
 ]
 
 
@@ -101,8 +115,9 @@ def test_planted_mistake_is_caught(desc, old, new, tmp_path):
     lib = oracle.load(oracle.compile_library(str(mutated), str(tmp_path / "libmutant.so")))
     failures = []
     for pin in oracle_pins.ALL_PINS:
-        if pin is oracle_pins.pin_half_exhaustive and "dec[" in old:
-            continue  # decode untouched: skip the slow exhaustive pin
+        if pin in (oracle_pins.pin_half_exhaustive, oracle_pins.pin_bf16_exhaustive) \
+                and ("dec[" in old or "gemm_full" in old or "gemm_elems" in old):
+            continue  # decode untouched: skip the slow exhaustive pins
         failures += pin(lib)
         if failures:
             break
