@@ -375,3 +375,35 @@ def test_non_default_stream():
         gemm.gemm_abt(At, Bt, C)
     s.synchronize()
     assert np.array_equal(C.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("name", ["1024^3", "4096x4096x1024", "2048x2048x16384"])
+def test_graph_replay(name):
+    """A call captured in a HIP graph (torch.cuda.CUDAGraph) replays to the eager
+    result, bitwise, on every replay, with eager work between replays. Split
+    plans use a caller workspace, allocated before capture."""
+    M, N, K = WORKLOADS.get(name) or inputs.PAGE_SHAPES[name]
+    A, B = operands((M, N, K), "uniform")
+    At, Bt = to_dev(A), to_dev(B)
+    eager = run(At, Bt)
+    nbytes = gemm.gemm_f16_f32_abt_workspace_size(M, N, K)
+    ws = (torch.empty((max(nbytes, 256) // 4,), dtype=torch.float32, device=DEV)
+          if nbytes else None)
+    C = torch.full((M, N), np.nan, dtype=torch.float32, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        gemm.gemm_abt(At, Bt, C, workspace=ws)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        gemm.gemm_abt(At, Bt, C, workspace=ws)
+    for r in range(3):
+        C.fill_(float("nan"))
+        if ws is not None:
+            ws.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(C.cpu().numpy(), eager), f"replay {r} differs"
+        run(At, Bt)  # eager work between replays
