@@ -258,6 +258,52 @@ def calibrate_copy(torch):
                       "launches": 5}), flush=True)
 
 
+def telemetry(torch, gemm, At, Bt, C, seconds=3.0):
+    """Clock and power while the GEMM runs back to back: amd-smi (a child
+    process) samples the board during a loop of calls. Context for reading the
+    power-limited clock, outside the timed region; None if amd-smi fails."""
+    import shutil
+    import subprocess
+
+    smi = shutil.which("amd-smi")
+    if smi is None:
+        return None
+    stream = torch.cuda.current_stream()
+
+    def burst():
+        for _ in range(8):
+            gemm.gemm_abt(At, Bt, C, stream=stream)
+        torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 1.0:  # reach the loaded clock first
+        burst()
+    proc = subprocess.Popen([smi, "metric", "-g", "0", "--power", "--clock", "--json"],
+                            stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    t0 = time.perf_counter()
+    while proc.poll() is None and time.perf_counter() - t0 < seconds:
+        burst()
+    try:
+        out, _ = proc.communicate(timeout=30)
+        d = json.loads(out)
+        gpu = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clocks = [v["clk"]["value"] for k, v in gpu["clock"].items()
+                  if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
+        power = gpu["power"]["socket_power"]["value"]
+        return {"gfx_clk_mhz": clocks, "socket_power_w": power,
+                "source": "amd-smi metric --power --clock, sampled during back-to-back calls"}
+    except Exception:  # noqa: BLE001 - telemetry is optional context
+        proc.kill()
+        return None
+
+
+def library_md5() -> str:
+    from dense_fp16_gemm_03_amd import gemm
+
+    with open(gemm.LIBRARY, "rb") as f:
+        return hashlib.md5(f.read()).hexdigest()
+
+
 def traffic_for(workload, kernel_avg_s):
     """HBM bytes per launch from committed rocprofv3 counters, if they match this source."""
     try:
@@ -281,6 +327,8 @@ def main():
     ap.add_argument("--workload", default="8192^3",
                     help="one of the five workloads, or one of the pages' other shapes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-telemetry", action="store_true",
+                    help="skip the amd-smi clock/power sample after the timed region")
     ap.add_argument("--shapes", action="store_true",
                     help="also time the five workloads, each call alone")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -381,6 +429,11 @@ def main():
     if args.vendor:
         vendor = vendor_arm(torch, gemm, list(inputs.WORKLOADS), dev)
 
+    tele = None if args.no_telemetry else telemetry(torch, gemm, At, Bt, C)
+    if tele is not None:
+        log(f"[bench] telemetry: gfx clocks {tele['gfx_clk_mhz']} MHz, "
+            f"socket power {tele['socket_power_w']} W")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU reference on a sample ...")
@@ -398,8 +451,8 @@ def main():
         "config": {"workload": f"gemm_abt {M}x{N}x{K}", "M": M, "N": N, "K": K,
                    "accumulate": "f32", "output": "f32",
                    "plan": gemm.gemm_f16_f32_abt_describe(M, N, K),
-                   "source_hash": source_hash()},
-        "roofline": roofline, "cpu_baseline": cpu, "shapes": shapes,
+                   "source_hash": source_hash(), "library_md5": library_md5()},
+        "roofline": roofline, "cpu_baseline": cpu, "shapes": shapes, "telemetry": tele,
     }
     if vendor is not None:
         line["vendor_hipblaslt"] = vendor
