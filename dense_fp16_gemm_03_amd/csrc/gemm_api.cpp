@@ -19,6 +19,10 @@ namespace {
 using namespace g16;
 
 constexpr int32_t kDefaultCUs = 256;  // MI355X: 8 XCDs x 32 CUs
+// Largest M, N or K accepted. The kernels index rows, columns and k in 32-bit
+// integers, and a tile's first index plus its extent (at most 256, plus the
+// ring's masked tail stages in k) must not pass 2^31 - 1.
+constexpr int64_t kMaxDim = 0x7FFFFFFF - 1024;
 // Kernel for large squares and for long K: 256x256 tiles, 16x16x32 MFMA,
 // two waves per SIMD in the ping-pong main loop.
 constexpr int32_t KID_LARGE = KID_256x256x32_S3_W8_M16_PP;
@@ -27,7 +31,7 @@ struct Plan {
   int32_t kid = -1;       // tiled kernel id, KID_GENERAL, or -1 (nothing to do)
   Sched s{};
   bool c_vec4 = false;
-  size_t workspace = 0;   // bytes of flags + counts (0 if the schedule needs none)
+  size_t workspace = 0;   // bytes of partial tiles (0 if the schedule needs none)
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -54,7 +58,7 @@ gemm_status_t validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t l
   if (K > 0 && (ranges_overlap(C, cbytes, A, span_bytes(M, lda, K, 2)) ||
                 ranges_overlap(C, cbytes, B, span_bytes(N, ldb, K, 2))))
     return GEMM_ERR_INVALID_VALUE;
-  if (M > 0x7FFFFFFF || N > 0x7FFFFFFF || K > 0x7FFFFFFF) return GEMM_ERR_NOT_SUPPORTED;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_ERR_NOT_SUPPORTED;
   if (((uintptr_t)A & 1) || ((uintptr_t)B & 1) || ((uintptr_t)C & 3))
     return GEMM_ERR_NOT_SUPPORTED;
   return GEMM_OK;
@@ -349,6 +353,7 @@ const char* gemm_status_string(gemm_status_t s) {
 gemm_status_t gemm_f16_f32_abt_describe(int64_t M, int64_t N, int64_t K, char* buf, size_t len) {
   if (buf == nullptr || len == 0) return GEMM_ERR_INVALID_VALUE;
   if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_VALUE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_ERR_NOT_SUPPORTED;
   const void* aligned = (const void*)(uintptr_t)256;
   const int64_t ld = K % 8 ? K + (8 - K % 8) : K;
   const Plan plan = make_plan(M, N, K, aligned, ld, aligned, ld, (const float*)aligned, N,

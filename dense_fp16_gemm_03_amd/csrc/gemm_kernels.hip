@@ -955,46 +955,50 @@ __global__ __launch_bounds__(kReduceThreads) void gemm_reduce_kernel(GemmParams 
                   tn * C::BN);
 }
 
-// General kernel: any shape, stride and (element-natural) alignment. One
-// workgroup of 4 waves per 64 x 64 tile of C, each wave a 32 x 32 block;
-// operands go straight from global memory into MFMA registers, element by
-// element with bounds checks. Slow; taken only when the tiled kernels'
-// alignment rules do not hold.
+// General kernel: any shape, stride and (element-natural) alignment. 4 waves
+// per 64 x 64 tile of C, each wave a 32 x 32 block; operands go straight from
+// global memory into MFMA registers, element by element with bounds checks.
+// Workgroups walk the tiles by stride, so the grid stays within the launch
+// limits however many tiles there are. Slow; taken only when the tiled
+// kernels' alignment rules do not hold.
 template <int DT>
-__global__ __launch_bounds__(256) void gemm_general_kernel(GemmParams p, int32_t tiles_n) {
+__global__ __launch_bounds__(256) void gemm_general_kernel(GemmParams p, int32_t tiles_n,
+                                                           int64_t tiles) {
   using M = Mma<32, DT>;
   typedef typename M::elem_t elem_t;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int tm = blockIdx.x / tiles_n;
-  const int tn = blockIdx.x % tiles_n;
-  const int m0 = tm * 64 + (wave >> 1) * 32;
-  const int n0 = tn * 64 + (wave & 1) * 32;
-  const int ar = m0 + (lane & 31);
-  const int br = n0 + (lane & 31);
-  const int kk = 8 * (lane >> 5);
-  const bool a_ok = ar < p.M;
-  const bool b_ok = br < p.N;
-  const uint16_t* arow = p.A + (int64_t)(a_ok ? ar : 0) * p.lda;
-  const uint16_t* brow = p.B + (int64_t)(b_ok ? br : 0) * p.ldb;
-  f32x16 acc = {};
-  for (int k0 = 0; k0 < p.K; k0 += 16) {
-    typename M::frag_t a, b;
+  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    const int tm = (int)(t / tiles_n);
+    const int tn = (int)(t % tiles_n);
+    const int m0 = tm * 64 + (wave >> 1) * 32;
+    const int n0 = tn * 64 + (wave & 1) * 32;
+    const int ar = m0 + (lane & 31);
+    const int br = n0 + (lane & 31);
+    const int kk = 8 * (lane >> 5);
+    const bool a_ok = ar < p.M;
+    const bool b_ok = br < p.N;
+    const uint16_t* arow = p.A + (int64_t)(a_ok ? ar : 0) * p.lda;
+    const uint16_t* brow = p.B + (int64_t)(b_ok ? br : 0) * p.ldb;
+    f32x16 acc = {};
+    for (int k0 = 0; k0 < p.K; k0 += 16) {
+      typename M::frag_t a, b;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int k = k0 + kk + e;
-      const bool kin = k < p.K;
-      a[e] = __builtin_bit_cast(elem_t, (a_ok && kin) ? arow[k] : (uint16_t)0);
-      b[e] = __builtin_bit_cast(elem_t, (b_ok && kin) ? brow[k] : (uint16_t)0);
+      for (int e = 0; e < 8; ++e) {
+        const int k = k0 + kk + e;
+        const bool kin = k < p.K;
+        a[e] = __builtin_bit_cast(elem_t, (a_ok && kin) ? arow[k] : (uint16_t)0);
+        b[e] = __builtin_bit_cast(elem_t, (b_ok && kin) ? brow[k] : (uint16_t)0);
+      }
+      acc = M::mma(b, a, acc);
     }
-    acc = M::mma(b, a, acc);
-  }
-  const int m = m0 + (lane & 31);
-  if (m < p.M) {
+    const int m = m0 + (lane & 31);
+    if (m < p.M) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int n = n0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (n < p.N) p.C[(int64_t)m * p.ldc + n] = acc[r];
+      for (int r = 0; r < 16; ++r) {
+        const int n = n0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (n < p.N) p.C[(int64_t)m * p.ldc + n] = acc[r];
+      }
     }
   }
 }
@@ -1116,15 +1120,18 @@ int32_t tiled_occupancy(int32_t kid) {
 hipError_t launch_general(int32_t dt, const GemmParams& p, hipStream_t stream) {
   const int64_t tiles_m = (p.M + 63) / 64;
   const int64_t tiles_n = (p.N + 63) / 64;
-  const int64_t blocks = tiles_m * tiles_n;
-  if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int64_t tiles = tiles_m * tiles_n;
+  if (tiles <= 0) return hipSuccess;
+  // A dispatch counts its work-items in 32 bits: cap the grid (2^20
+  // workgroups of 256, far more than fit on the chip at once) and let
+  // workgroups take further tiles by stride.
+  const uint32_t grid = (uint32_t)min_of<int64_t>(tiles, (int64_t)1 << 20);
   if (dt == DT_BF16)
-    hipLaunchKernelGGL(gemm_general_kernel<DT_BF16>, dim3((uint32_t)blocks), dim3(256), 0, stream,
-                       p, (int32_t)tiles_n);
+    hipLaunchKernelGGL(gemm_general_kernel<DT_BF16>, dim3(grid), dim3(256), 0, stream, p,
+                       (int32_t)tiles_n, tiles);
   else
-    hipLaunchKernelGGL(gemm_general_kernel<DT_F16>, dim3((uint32_t)blocks), dim3(256), 0, stream,
-                       p, (int32_t)tiles_n);
+    hipLaunchKernelGGL(gemm_general_kernel<DT_F16>, dim3(grid), dim3(256), 0, stream, p,
+                       (int32_t)tiles_n, tiles);
   return hipGetLastError();
 }
 

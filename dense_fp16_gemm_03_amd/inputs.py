@@ -18,6 +18,10 @@ k-block-weighted ones pattern) give closed-form products for the pins.
 
 Standard seeds: A = 1, B = 2 for ``uniform``; A = 3, B = 4 for ``integer``.
 
+``device_uniform`` draws multi-gigabyte operands on the GPU with torch's
+seeded generator instead (same distribution, binary32 draws rounded to
+binary16); the reference then reads back the rows it checks.
+
 bfloat16 operands are numpy ``uint16`` arrays of bfloat16 bit patterns (numpy
 has no bfloat16 type): the same draws, rounded binary64 -> binary32 -> bfloat16,
 each step to nearest-even (``to_bf16_bits``). Integers up to 256 in magnitude
@@ -85,6 +89,32 @@ def hash_int(rows: int, cols: int, salt: int = 0) -> np.ndarray:
         h = _splitmix64(idx)
     v = (h % np.uint64(7)).astype(np.int64) - 3
     return v.reshape(rows, cols).astype(np.float16)
+
+
+def device_uniform(rows: int, cols: int, seed: int, device, ld: int | None = None):
+    """rows x cols binary16 torch tensor on `device`, i.i.d. uniform on [-1, 1]:
+    binary32 draws on [-1, 1) from torch's seeded generator for that device,
+    rounded to binary16.
+
+    For operands too large to draw on the host (gigabytes); whoever checks a
+    result copies back the rows it needs. With ld > cols the tensor is a view
+    of a rows x ld buffer whose columns past `cols` hold NaN, so a read beyond
+    K poisons the result.
+    """
+    import torch
+
+    ld = cols if ld is None else ld
+    if ld < cols:
+        raise ValueError("ld must be >= cols")
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    if ld == cols:
+        buf = torch.empty((rows, ld), dtype=torch.float16, device=device)
+    else:
+        buf = torch.full((rows, ld), float("nan"), dtype=torch.float16, device=device)
+    view = buf[:, :cols]
+    view.uniform_(-1.0, 1.0, generator=gen)
+    return view
 
 
 def identity(n: int, cols: int | None = None) -> np.ndarray:

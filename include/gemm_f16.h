@@ -44,6 +44,8 @@ typedef enum {
 /* C = A * B^T (see the layout block above). A, B, C are device pointers.
  * Requirements: M, N, K >= 0; lda >= K; ldb >= K; ldc >= N; A, B, C non-NULL
  * when M*N > 0 (A, B may be NULL when K = 0); C must not overlap A or B.
+ * M, N and K above 2147482623 (2^31 - 1025; the kernels index in 32 bits)
+ * return GEMM_ERR_NOT_SUPPORTED; strides and byte sizes may exceed 2^31.
  * Any alignment of pointers and strides is accepted: 16-byte aligned A, B
  * with lda, ldb, K multiples of 8 take the tiled MFMA kernels, anything else
  * a slower general kernel. Split-K / stream-K plans write fp32 partial tiles
@@ -98,7 +100,8 @@ gemm_status_t gemm_bf16_f32_abt_ws(int64_t M, int64_t N, int64_t K,
 const char* gemm_status_string(gemm_status_t s);
 
 /* Writes a one-line description of the plan chosen for (M, N, K) into the
- * host buffer buf (NUL-terminated, truncated to len). Touches no device. */
+ * host buffer buf (NUL-terminated, truncated to len). Touches no device.
+ * Same size limits as gemm_f16_f32_abt (GEMM_ERR_NOT_SUPPORTED beyond them). */
 gemm_status_t gemm_f16_f32_abt_describe(int64_t M, int64_t N, int64_t K, char* buf, size_t len);
 
 /* Frees the library-owned workspaces of the current device after waiting for

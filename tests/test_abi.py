@@ -42,6 +42,7 @@ def test_status_strings(lib):
 
 # Fake device addresses: validation never dereferences them.
 A_PTR, B_PTR, C_PTR = 0x10000000, 0x20000000, 0x30000000
+MAX_DIM = (1 << 31) - 1025  # largest M, N or K the library takes
 
 
 @pytest.mark.parametrize("args,expect", [
@@ -57,6 +58,9 @@ A_PTR, B_PTR, C_PTR = 0x10000000, 0x20000000, 0x30000000
     ((4, 4, 8, A_PTR + 1, 8, B_PTR, 8, C_PTR, 4), 2),       # A not 2-byte aligned
     ((4, 4, 8, A_PTR, 8, B_PTR, 8, C_PTR + 2, 4), 2),       # C not 4-byte aligned
     ((1 << 31, 4, 8, A_PTR, 8, B_PTR, 8, 1 << 44, 4), 2),   # M too large
+    ((MAX_DIM + 1, 4, 8, A_PTR, 8, B_PTR, 8, 1 << 44, 4), 2),  # M one past the limit
+    ((4, MAX_DIM + 1, 8, A_PTR, 8, B_PTR, 8, 1 << 44, MAX_DIM + 1), 2),  # N past it
+    ((4, 4, MAX_DIM + 1, A_PTR, MAX_DIM + 1, 1 << 40, MAX_DIM + 1, 1 << 44, 4), 2),  # K
     ((0, 4, 8, A_PTR, 8, B_PTR, 8, C_PTR, 4), 0),           # M = 0: nothing to do
     ((4, 0, 8, 0, 8, 0, 8, 0, 0), 0),                       # N = 0: nothing to do
 ])
@@ -104,6 +108,14 @@ def test_describe_workloads(lib, name):
     M, N, K = inputs.WORKLOADS[name]
     text = gemm.gemm_f16_f32_abt_describe(M, N, K)
     assert f"M={M} N={N} K={K}" in text and "kernel=" in text
+
+
+def test_describe_size_limit(lib):
+    for M, N, K in ((MAX_DIM, 1, 8), (1, MAX_DIM, 8), (1, 1, MAX_DIM)):
+        assert f"M={M} N={N} K={K}" in gemm.gemm_f16_f32_abt_describe(M, N, K)
+    for M, N, K in ((MAX_DIM + 1, 1, 8), (1, MAX_DIM + 1, 8), (1, 1, MAX_DIM + 1)):
+        with pytest.raises(gemm.GemmError, match="NOT_SUPPORTED"):
+            gemm.gemm_f16_f32_abt_describe(M, N, K)
 
 
 def test_describe_general_and_empty(lib):
