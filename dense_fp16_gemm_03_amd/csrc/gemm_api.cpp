@@ -203,11 +203,11 @@ const char* mode_name(int32_t m) {
 }
 
 // Device CU counts, cached per device.
-std::mutex g_mu;
+std::mutex g_cus_mu;
 std::map<int, int32_t> g_cus;
 
 int32_t device_cus(int dev) {
-  std::lock_guard<std::mutex> lock(g_mu);
+  std::lock_guard<std::mutex> lock(g_cus_mu);
   auto it = g_cus.find(dev);
   if (it != g_cus.end()) return it->second;
   int n = 0;
@@ -218,15 +218,18 @@ int32_t device_cus(int dev) {
 }
 
 // Library-owned workspaces (partial tiles of split-K / stream-K plans), one
-// per (device, stream).
+// per (device, stream). g_ws_mu is held from taking a workspace until the
+// kernels that use it are enqueued, so a call from another host thread that
+// grows the same workspace cannot free it in between.
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
+std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
+// The caller holds g_ws_mu.
 gemm_status_t library_workspace(int dev, hipStream_t stream, size_t need, void** out) {
-  std::lock_guard<std::mutex> lock(g_mu);
   Workspace& w = g_ws[{dev, stream}];
   if (w.bytes >= need) {
     *out = w.ptr;
@@ -280,6 +283,7 @@ gemm_status_t run(int32_t dt, int64_t M, int64_t N, int64_t K, const void* A, in
   if (plan.kid == KID_GENERAL) {
     return launch_general(dt, p, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
   }
+  std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);
   if (plan.workspace > 0) {
     void* w = nullptr;
     if (caller_ws) {
@@ -287,6 +291,7 @@ gemm_status_t run(int32_t dt, int64_t M, int64_t N, int64_t K, const void* A, in
         return GEMM_ERR_WORKSPACE;
       w = ws;
     } else {
+      ws_lock.lock();  // released once the kernels are enqueued
       st = library_workspace(dev, stream, plan.workspace, &w);
       if (st != GEMM_OK) return st;
     }
@@ -380,7 +385,7 @@ gemm_status_t gemm_f16_f32_abt_describe(int64_t M, int64_t N, int64_t K, char* b
 void gemm_f16_release_workspaces(void) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return;
-  std::lock_guard<std::mutex> lock(g_mu);
+  std::lock_guard<std::mutex> lock(g_ws_mu);
   for (auto it = g_ws.begin(); it != g_ws.end();) {
     if (it->first.first == dev) {
       (void)hipStreamSynchronize(it->first.second);
@@ -395,6 +400,7 @@ void gemm_f16_release_workspaces(void) {
 int64_t gemm_f16_schedule_dump(int64_t M, int64_t N, int64_t K, int64_t grid, int64_t* out,
                                int64_t cap, int64_t* k_iters, int64_t* tiles) {
   if (M <= 0 || N <= 0 || K <= 0 || cap < 0 || (cap > 0 && out == nullptr)) return -1;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return -1;
   const void* aligned = (const void*)(uintptr_t)256;
   const int64_t ld = K % 8 ? K + (8 - K % 8) : K;
   Plan plan = make_plan(M, N, K, aligned, ld, aligned, ld, (const float*)aligned, N, kDefaultCUs);

@@ -53,7 +53,8 @@ typedef enum {
  * (k) order, into C, so results do not depend on timing. The workspace is
  * library-owned, allocated once per (device, stream) on first use and grown
  * when a larger one is needed; calls sharing a stream are ordered by it,
- * calls on different streams do not share one. */
+ * calls on different streams do not share one. Calls from several host
+ * threads at once are safe, on one stream or on several. */
 gemm_status_t gemm_f16_f32_abt(int64_t M, int64_t N, int64_t K,
                                const void* A, int64_t lda,
                                const void* B, int64_t ldb,

@@ -377,6 +377,48 @@ def test_non_default_stream():
     assert np.array_equal(C.cpu().numpy(), ref)
 
 
+def test_threads_share_a_stream():
+    """Two host threads call the library at once on the same (null) stream,
+    each with a split plan of a different workspace size, starting from no
+    workspace: one grows the stream's workspace while the other uses it.
+    Every result equals the single-threaded one bit for bit."""
+    import threading
+
+    shapes = [(512, 512, 8192), (256, 256, 65536)]  # splits 4 and 32
+    ops, refs = [], []
+    for i, (M, N, K) in enumerate(shapes):
+        A, B = inputs.uniform(M, K, 61 + i), inputs.uniform(N, K, 71 + i)
+        ref, S = oracle.gemm_abt(A, B)
+        At, Bt = to_dev(A), to_dev(B)
+        single = run(At, Bt)
+        assert_tol(single, ref, S, f"{M}x{N}x{K} single-threaded")
+        ops.append((At, Bt))
+        refs.append(single)
+    torch.cuda.synchronize()
+    gemm.gemm_f16_release_workspaces()
+    outs = [[torch.full((M, N), np.nan, dtype=torch.float32, device=DEV) for _ in range(8)]
+            for (M, N, K) in shapes]
+    errors = []
+
+    def worker(i):
+        try:
+            for C in outs[i]:
+                gemm.gemm_abt(*ops[i], C)
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(shapes))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i, Cs in enumerate(outs):
+        for C in Cs:
+            assert np.array_equal(C.cpu().numpy(), refs[i]), f"shape {shapes[i]}"
+
+
 @pytest.mark.parametrize("name", ["1024^3", "4096x4096x1024", "2048x2048x16384"])
 def test_graph_replay(name):
     """A call captured in a HIP graph (torch.cuda.CUDAGraph) replays to the eager
