@@ -147,7 +147,10 @@ def gemm_abt(A, B, C=None, stream=None, workspace=None):
     """C = A @ B^T for torch tensors: A (M, K) and B (N, K) both float16 or
     both bfloat16, C (M, N) float32, all on one GPU with unit stride along the
     last dimension. Returns C. Enqueued on ``stream`` (default: torch's
-    current stream)."""
+    current stream). ``workspace``, if given, is a contiguous tensor on the
+    same GPU of at least ``gemm_f16_f32_abt_workspace_size(M, N, K)`` bytes,
+    256-byte aligned (the ``_ws`` entry points); otherwise the library uses
+    its own per-stream workspace."""
     import torch
 
     if A.dtype != B.dtype or A.dtype not in (torch.float16, torch.bfloat16):
@@ -166,6 +169,9 @@ def gemm_abt(A, B, C=None, stream=None, workspace=None):
             raise ValueError(f"{name} must be on A's GPU")
         if t.shape[1] > 1 and t.stride(1) != 1 and t.numel() > 0:
             raise ValueError(f"{name} must have unit stride along its last dimension")
+    if workspace is not None and (not workspace.is_cuda or workspace.device != A.device
+                                  or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on A's GPU")
     lda = A.stride(0) if M > 1 else max(K, 1)
     ldb = B.stride(0) if N > 1 else max(K, 1)
     ldc = C.stride(0) if M > 1 else max(N, 1)

@@ -377,6 +377,20 @@ def test_non_default_stream():
     assert np.array_equal(C.cpu().numpy(), ref)
 
 
+def test_workspace_must_be_on_the_gpu():
+    M, N, K = WORKLOADS["2048x2048x16384"]
+    A = torch.zeros((M, K), dtype=torch.float16, device=DEV)
+    B = torch.zeros((N, K), dtype=torch.float16, device=DEV)
+    C = torch.full((M, N), np.nan, dtype=torch.float32, device=DEV)
+    need = gemm.gemm_f16_f32_abt_workspace_size(M, N, K)
+    for ws in (torch.empty(need, dtype=torch.uint8),  # host memory
+               torch.empty(2 * need, dtype=torch.uint8, device=DEV)[::2]):  # strided
+        with pytest.raises(ValueError, match="workspace"):
+            gemm.gemm_abt(A, B, C, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(C).all()  # rejected before any launch
+
+
 def test_threads_share_a_stream():
     """Two host threads call the library at once on the same (null) stream,
     each with a split plan of a different workspace size, starting from no
