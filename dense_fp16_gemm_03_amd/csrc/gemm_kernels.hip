@@ -11,18 +11,19 @@
 //     that page's TMA section).
 //   * a ring of STAGES such buffers: loads for k-iteration i+STAGES-1 are in
 //     flight while iteration i computes; a wait on the load counter plus a
-//     workgroup barrier hands a stage over, and the tail waits on fewer loads
-//     when no more are issued (the "commit empty groups" rule of that page).
+//     workgroup barrier hands a stage over. Past the end of K the ring still
+//     issues (fully masked) loads, so every wait counts the same number of
+//     loads; that page makes its pipeline's group count uniform the same way.
 //   * LDS -> registers with ds_read_b128 (8 halves a lane) and an fp16 MFMA
 //     (v_mfma_f32_32x32x16_f16 or v_mfma_f32_16x16x32_f16) into per-wave
 //     register-blocked accumulators. The next stage is handed over before the
 //     last k-step's MFMAs are issued, so its first fragments load while those
-//     MFMAs run ("asking a stage ahead" in "SASS-Level Kernel Generation for
-//     Blackwell", section "Inside the kernels").
+//     MFMAs run (requesting data one stage early, as "SASS-Level Kernel
+//     Generation for Blackwell" does, section "Inside the kernels").
 //   * the B tile is fed as the MFMA's first operand and the A tile as its
 //     second (SwapAB in the same section), so each lane ends up holding runs
 //     of 4 consecutive columns of C and stores them as one 16-byte write,
-//     straight from the registers ("stored from the registers").
+//     straight from the registers with no staging through LDS.
 //   * split-K / stream-K (section "Inside the kernels", where the shares of a
 //     tile are added in the L2): a tile whose k-iterations are shared among
 //     workgroups is not added in place. Every share writes its fp32 partial

@@ -4,22 +4,21 @@
 // is the very code the kernels run.
 //
 // Three modes, after the per-shape program rule of "SASS-Level Kernel
-// Generation for Blackwell" (section "Inside the kernels"):
+// Generation for Blackwell" (section "Inside the kernels"), which picks for
+// each shape between a persistent grid over whole tiles, a split of K and
+// stream-K:
 //   DATA_PARALLEL  each output tile is one unit over all of K; a fixed grid
-//                  walks the units by stride ("a fixed grid ... walking the
-//                  tiles by stride").
-//   SPLIT          K of every tile is cut into `splits` even shares ("K split
-//                  ... ways over the grid, adding in the L2").
-//   STREAM_K       the tiles' k-iterations, laid end to end, are cut into one
-//                  contiguous range per workgroup ("stream-K ... the CTA
-//                  holding a tile's first k step stores it, and the tile's
-//                  other CTAs add to it").
-// A tile whose k-iterations are shared among several workgroups is reduced
-// through the workspace: every share writes its fp32 partial tile, and once
-// all shares of the tile have arrived each one sums a slice of the tile over
-// all partials, in k order, and writes that slice of C. Shared tiles occur
-// only in schedules where all of a tile's shares run at once (one unit per
-// workgroup in SPLIT; one range per workgroup in STREAM_K).
+//                  of workgroups takes the units by stride.
+//   SPLIT          the k-iterations of every tile are cut into `splits`
+//                  contiguous, near-equal shares, each its own unit.
+//   STREAM_K       the k-iterations of all tiles, laid end to end, are cut
+//                  into one contiguous range per workgroup; a range may end
+//                  part-way through a tile and start the next one.
+// The shares of a tile are not added in place (the page adds them in L2):
+// each share writes its fp32 partial tile to a workspace slot, and a reduce
+// kernel launched after the main kernel on the same stream sums every tile's
+// slots in k order and writes C. Nothing in the schedule requires the shares
+// of a tile to run at the same time.
 #pragma once
 
 #include <stdint.h>
@@ -47,7 +46,7 @@ struct Sched {
 };
 
 struct Segment {
-  int32_t tile;        // position in tile order (also the flag index)
+  int32_t tile;        // position in tile order (also the partial-tile slot group)
   int32_t tm, tn;      // tile coordinates
   int32_t k_begin;     // first k-iteration (inclusive)
   int32_t k_end;       // last k-iteration (exclusive)
