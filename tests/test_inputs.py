@@ -1,5 +1,6 @@
 """Seeded synthetic operands: determinism and value sets (CPU only)."""
 import numpy as np
+import pytest
 
 from dense_fp16_gemm_03_amd import inputs
 
@@ -88,3 +89,22 @@ def test_bf16_generators():
     assert np.array_equal(_bf16_values(p).astype(np.int64), ((37 * j + 11 * k) % 256) - 128)
     A, B = inputs.workload_operands((64, 32, 16), "hash_int", "bf16")
     assert np.array_equal(_bf16_values(A), inputs.hash_int(64, 16, 1).astype(np.float32))
+
+
+def test_device_uniform_on_the_cpu_generator():
+    """The device-side generator, run on torch's CPU device: seeded, in
+    [-1, 1], padding columns NaN, rows contiguous with stride ld."""
+    import torch
+
+    a = inputs.device_uniform(50, 40, 7, "cpu")
+    assert a.dtype == torch.float16 and tuple(a.shape) == (50, 40) and a.is_contiguous()
+    assert torch.equal(a, inputs.device_uniform(50, 40, 7, "cpu"))
+    assert not torch.equal(a, inputs.device_uniform(50, 40, 8, "cpu"))
+    v = a.float()
+    assert v.min().item() >= -1 and v.max().item() <= 1 and v.std().item() > 0.5
+    p = inputs.device_uniform(50, 40, 7, "cpu", ld=56)
+    assert p.stride() == (56, 1)
+    full = p.as_strided((50, 56), (56, 1))
+    assert torch.isnan(full[:, 40:]).all() and not torch.isnan(p).any()
+    with pytest.raises(ValueError):
+        inputs.device_uniform(4, 8, 1, "cpu", ld=7)
