@@ -1,0 +1,55 @@
+"""bench.py's host logic without a GPU: the multi-GPU refusal, the algorithmic
+figures, the traffic lookup keyed by the source hash and the CPU baseline leg."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from dense_fp16_gemm_03_amd import inputs  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_algorithmic_figures():
+    flops, nbytes = bench.algorithmic(8192, 8192, 8192)
+    assert flops == 2.0 * 8192**3
+    assert nbytes == 2.0 * (2 * 8192 * 8192) + 4.0 * 8192 * 8192  # A, B read once, C written once
+    assert bench.algorithmic(1024, 1024, 65536) == (2.0 * 1024 * 1024 * 65536,
+                                                    2.0 * 2 * 1024 * 65536 + 4.0 * 1024 * 1024)
+
+
+def test_traffic_needs_the_current_source(tmp_path, monkeypatch):
+    good = tmp_path / "traffic.json"
+    good.write_text(json.dumps({"8192^3": {"source_hash": bench.source_hash(),
+                                           "bytes_per_launch": 123}}))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(good))
+    assert bench.traffic_for("8192^3", 1e-3) == 123
+    assert bench.traffic_for("1024^3", 1e-3) is None
+    stale = tmp_path / "stale.json"
+    stale.write_text(json.dumps({"8192^3": {"source_hash": "0" * 16, "bytes_per_launch": 123}}))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(stale))
+    assert bench.traffic_for("8192^3", 1e-3) is None
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
+    assert bench.traffic_for("8192^3", 1e-3) is None
+
+
+def test_cpu_baseline_record():
+    M, N, K = 64, 48, 32
+    A, B = inputs.uniform(M, K, 1), inputs.uniform(N, K, 2)
+    r = bench.cpu_baseline(A, B, M, N, K, budget_s=0.05)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["cores"] >= 1
+    assert r["value"] > 0 and "rows 0.." in r["sample"]
+    Ab = inputs.uniform_bf16(M, K, 1)
+    Bb = inputs.uniform_bf16(N, K, 2)
+    assert np.isfinite(bench.cpu_baseline(Ab, Bb, M, N, K, budget_s=0.05)["value"])
