@@ -1,0 +1,100 @@
+"""Seeded random cases (needs an MI355X).
+
+Each case draws, from one fixed seed, a shape (M, N up to 700, K up to 2200),
+row strides and pointer offsets for A, B and C, the operand type (binary16 or
+bfloat16) and a forced plan (kernel id, data-parallel / split-K / stream-K,
+grid). Inputs are integers in {-2..2}, where every partial sum is exact in
+fp32, so C must equal the CPU reference bit for bit whatever the summation
+order. C sits inside a NaN-filled buffer with padding columns on both sides:
+after the call the padding must still be NaN (no store outside C).
+
+About a quarter of the cases use unaligned pointers or strides, which the
+plan rule sends to the general kernel; the rest take the forced tiled kernel.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from dense_fp16_gemm_03_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+from dense_fp16_gemm_03_amd import gemm  # noqa: E402
+
+DEV = torch.device("cuda:0")
+SEED = 20261202
+N_CASES = 200
+KIDS_F16 = 35
+KIDS_BF16 = (16, 18, 25, 26, 27)
+
+
+def draw(i):
+    rng = np.random.default_rng([SEED, i])
+    M, N, K = int(rng.integers(1, 701)), int(rng.integers(1, 701)), int(rng.integers(1, 2201))
+    aligned = rng.random() < 0.75
+    if aligned:
+        K = max(8, K // 8 * 8)
+        pad_a, pad_b = (int(rng.choice([0, 8, 40, 128])) for _ in range(2))
+        off_a = off_b = 0
+    else:
+        pad_a, pad_b = int(rng.integers(0, 9)), int(rng.integers(0, 9))
+        off_a, off_b = int(rng.integers(0, 8)), int(rng.integers(0, 8))
+    pad_c = int(rng.choice([0, 1, 3, 4, 12]))
+    off_c = int(rng.choice([0, 1, 2, 4]))
+    dtype = "bf16" if rng.random() < 0.4 else "f16"
+    kid = int(rng.choice(KIDS_BF16)) if dtype == "bf16" else int(rng.integers(0, KIDS_F16))
+    plan = f"kid={kid}"
+    mode = int(rng.integers(0, 3))
+    if mode == 1:
+        plan += f",mode=1,splits={int(rng.integers(2, 9))}"
+    elif mode == 2:
+        plan += ",mode=2"
+    if rng.random() < 0.5:
+        plan += f",grid={int(rng.integers(1, 300))}"
+    return dict(M=M, N=N, K=K, pad_a=pad_a, pad_b=pad_b, off_a=off_a, off_b=off_b,
+                pad_c=pad_c, off_c=off_c, dtype=dtype, plan=plan)
+
+
+def operand(bits_or_half, off, pad, dtype):
+    """Device view of the operand inside a larger buffer (offset `off`
+    elements into each row, `pad` spare elements after it)."""
+    rows, cols = bits_or_half.shape
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(bits_or_half).view(np.int16)).view(torch.bfloat16)
+        tdt = torch.bfloat16
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(bits_or_half))
+        tdt = torch.float16
+    buf = torch.zeros((rows, off + cols + pad), dtype=tdt, device=DEV)
+    buf[:, off:off + cols] = t.to(DEV)
+    return buf[:, off:off + cols]
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_case(i, monkeypatch):
+    c = draw(i)
+    print(f"[gpu test] random case {i}: {c}", flush=True)
+    monkeypatch.setenv("GEMM_F16_PLAN", c["plan"])
+    M, N, K = c["M"], c["N"], c["K"]
+    if c["dtype"] == "bf16":
+        A, B = inputs.integer_bf16(M, K, 1000 + i), inputs.integer_bf16(N, K, 2000 + i)
+        ref, _ = oracle.gemm_abt_bf16(A, B)
+    else:
+        A, B = inputs.integer(M, K, 1000 + i), inputs.integer(N, K, 2000 + i)
+        ref, _ = oracle.gemm_abt(A, B)
+    Av = operand(A, c["off_a"], c["pad_a"], c["dtype"])
+    Bv = operand(B, c["off_b"], c["pad_b"], c["dtype"])
+    off_c, pad_c = c["off_c"], c["pad_c"]
+    Cbuf = torch.full((M, off_c + N + pad_c), float("nan"), dtype=torch.float32, device=DEV)
+    gemm.gemm_abt(Av, Bv, Cbuf[:, off_c:off_c + N])
+    torch.cuda.synchronize()
+    out = Cbuf.cpu().numpy()
+    got = out[:, off_c:off_c + N].astype(np.float64)
+    bad = got != ref
+    assert not bad.any(), f"case {i}: {bad.sum()} mismatches, first at {np.argwhere(bad)[:3].tolist()}"
+    assert np.isnan(out[:, :off_c]).all() and np.isnan(out[:, off_c + N:]).all(), \
+        f"case {i}: a store landed outside C"
