@@ -27,12 +27,22 @@ constexpr int64_t kMaxDim = 0x7FFFFFFF - 1024;
 // two waves per SIMD in the ping-pong main loop.
 constexpr int32_t KID_LARGE = KID_256x256x32_S3_W8_M16_PP;
 
+// Smallest product (M*N*K multiply-adds) for which operands the tiled
+// kernels cannot load directly are packed first; below it the general kernel
+// is as fast as the extra pack launches.
+constexpr double kPackMinWork = (double)(1 << 22);
+
 struct Plan {
   int32_t kid = -1;       // tiled kernel id, KID_GENERAL, or -1 (nothing to do)
   Sched s{};
   bool c_vec4 = false;
-  size_t workspace = 0;   // bytes of partial tiles (0 if the schedule needs none)
+  size_t workspace = 0;   // bytes: partial tiles, then packed operands (0 if none)
+  size_t partial_bytes = 0;  // the partial tiles at the start of the workspace
+  bool pack_a = false, pack_b = false;  // operand copied to aligned rows first
+  int64_t kp = 0;         // K of the packed operands (K rounded up to 8)
 };
+
+size_t round256(int64_t bytes) { return (size_t)((bytes + 255) / 256 * 256); }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -68,6 +78,7 @@ gemm_status_t validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t l
 // (any subset of keys). Read on every plan; unknown keys are ignored.
 struct Override {
   int32_t kid = -1, mode = -1, splits = -1, grid = -1, group = -1, xcd = -1;
+  int32_t general = 0;  // 1: the general kernel, whatever the operands
 };
 
 Override read_override() {
@@ -86,23 +97,27 @@ Override read_override() {
     else if (!std::strcmp(key, "grid")) o.grid = val;
     else if (!std::strcmp(key, "group")) o.group = val;
     else if (!std::strcmp(key, "xcd")) o.xcd = val;
+    else if (!std::strcmp(key, "general")) o.general = val;
   }
   return o;
+}
+
+// True when the tiled kernels can load an operand directly: 16-byte aligned
+// rows of a multiple of 8 elements, and buffer offsets within a tile of
+// `tile_rows` rows (row * ld + k, in bytes) below 2^31.
+bool operand_loadable(const void* X, int64_t ld, int64_t K, int32_t tile_rows, int32_t bk) {
+  if (((uintptr_t)X & 15) || ld % 8 || K % 8) return false;
+  const int64_t limit = (int64_t)1 << 31;
+  return (int64_t)(tile_rows - 1) * ld * 2 + (K + bk) * 2 < limit;
 }
 
 bool tiled_eligible(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                     int64_t ldb, int32_t kid) {
   const KernelInfo* ki = kernel_info(kid);
   if (!ki || K <= 0) return false;
-  if (((uintptr_t)A & 15) || ((uintptr_t)B & 15)) return false;
-  if (lda % 8 || ldb % 8 || K % 8) return false;
-  // Buffer offsets (row * ld + k, in bytes) must stay below 2^31.
-  const int64_t limit = (int64_t)1 << 31;
-  if ((int64_t)(ki->bm - 1) * lda * 2 + (K + ki->bk) * 2 >= limit) return false;
-  if ((int64_t)(ki->bn - 1) * ldb * 2 + (K + ki->bk) * 2 >= limit) return false;
   (void)M;
   (void)N;
-  return true;
+  return operand_loadable(A, lda, K, ki->bm, ki->bk) && operand_loadable(B, ldb, K, ki->bn, ki->bk);
 }
 
 // Shape -> kernel and schedule. The pages' rule (section "Inside the kernels"
@@ -117,11 +132,47 @@ bool tiled_eligible(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
 //     would fill fewer than half the CUs, data-parallel (at these sizes the
 //     reduce pass of a split costs more than it gains).
 Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-               int64_t ldb, const float* C, int64_t ldc, int32_t cus, int32_t dt = DT_F16) {
+               int64_t ldb, const float* C, int64_t ldc, int32_t cus, int32_t dt = DT_F16,
+               bool allow_pack = true);
+
+// Operands the tiled kernels cannot load directly (a pointer off 16 bytes, a
+// row stride or K not a multiple of 8, a stride past the offset limit): for a
+// large enough product each such operand is first copied into rows of K
+// rounded up to 8 elements, zero-filled past K, at the end of the workspace,
+// and the tiled plan runs on the copies. Otherwise the general kernel.
+Plan packed_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                 int64_t ldb, const float* C, int64_t ldc, int32_t cus, int32_t dt, int32_t kid) {
+  Plan general;
+  general.kid = KID_GENERAL;
+  if (K <= 0 || (double)M * (double)N * (double)K < kPackMinWork) return general;
+  const KernelInfo* ki = kernel_info(kid);
+  const int64_t kp = cdiv(K, 8) * 8;
+  const bool pa = !operand_loadable(A, lda, K, ki->bm, ki->bk);
+  const bool pb = !operand_loadable(B, ldb, K, ki->bn, ki->bk);
+  const void* aligned = (const void*)(uintptr_t)256;
+  Plan p = make_plan(M, N, kp, pa ? aligned : A, pa ? kp : lda, pb ? aligned : B,
+                     pb ? kp : ldb, C, ldc, cus, dt, false);
+  if (p.kid < 0 || p.kid == KID_GENERAL) return general;
+  p.pack_a = pa;
+  p.pack_b = pb;
+  p.kp = kp;
+  p.partial_bytes = p.workspace;
+  if (pa) p.workspace += round256(M * kp * 2);
+  if (pb) p.workspace += round256(N * kp * 2);
+  return p;
+}
+
+Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+               int64_t ldb, const float* C, int64_t ldc, int32_t cus, int32_t dt,
+               bool allow_pack) {
   Plan plan;
   if (M == 0 || N == 0) return plan;
   plan.c_vec4 = ((uintptr_t)C % 16 == 0) && (ldc % 4 == 0);
   const Override o = read_override();
+  if (o.general == 1) {
+    plan.kid = KID_GENERAL;
+    return plan;
+  }
 
   int32_t kid = KID_LARGE;
   int32_t mode = MODE_DATA_PARALLEL;
@@ -147,6 +198,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
   if (o.splits >= 1) splits = o.splits;
 
   if (!tiled_eligible(M, N, K, A, lda, B, ldb, kid)) {
+    if (allow_pack) return packed_plan(M, N, K, A, lda, B, ldb, C, ldc, cus, dt, kid);
     plan.kid = KID_GENERAL;
     return plan;
   }
@@ -244,11 +296,32 @@ gemm_status_t library_workspace(int dev, hipStream_t stream, size_t need, void**
   }
   size_t bytes = need < 65536 ? 65536 : need;
   void* p = nullptr;
-  if (hipMalloc(&p, bytes) != hipSuccess) return GEMM_ERR_ALLOC;
+  if (hipMalloc(&p, bytes) != hipSuccess) {
+    (void)hipGetLastError();  // clear it, so a later launch check does not report it
+    return GEMM_ERR_ALLOC;
+  }
   w.ptr = p;
   w.bytes = bytes;
   *out = p;
   return GEMM_OK;
+}
+
+bool workspace_fits(const Plan& plan, const void* ws, size_t ws_bytes) {
+  return plan.workspace == 0 || (ws != nullptr && ws_bytes >= plan.workspace &&
+                                 ((uintptr_t)ws & 255) == 0);
+}
+
+// The plan for a call with a caller workspace: a plan that packs operands but
+// does not fit the workspace runs the general kernel instead (packing is an
+// optimisation; partial tiles are not).
+Plan caller_plan(Plan plan, const void* ws, size_t ws_bytes) {
+  if ((plan.pack_a || plan.pack_b) && !workspace_fits(plan, ws, ws_bytes)) {
+    Plan general;
+    general.kid = KID_GENERAL;
+    general.c_vec4 = plan.c_vec4;
+    return general;
+  }
+  return plan;
 }
 
 gemm_status_t run(int32_t dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
@@ -261,13 +334,13 @@ gemm_status_t run(int32_t dt, int64_t M, int64_t N, int64_t K, const void* A, in
   int dev = 0;
   if (caller_ws) {
     // Checks on the caller's workspace come before any HIP call.
-    const Plan probe = make_plan(M, N, K, A, lda, B, ldb, C, ldc, kDefaultCUs, dt);
-    if (probe.workspace > 0 && (ws == nullptr || ws_bytes < probe.workspace ||
-                                ((uintptr_t)ws & 255)))
-      return GEMM_ERR_WORKSPACE;
+    const Plan probe =
+        caller_plan(make_plan(M, N, K, A, lda, B, ldb, C, ldc, kDefaultCUs, dt), ws, ws_bytes);
+    if (!workspace_fits(probe, ws, ws_bytes)) return GEMM_ERR_WORKSPACE;
   }
   if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
-  const Plan plan = make_plan(M, N, K, A, lda, B, ldb, C, ldc, device_cus(dev), dt);
+  Plan plan = make_plan(M, N, K, A, lda, B, ldb, C, ldc, device_cus(dev), dt);
+  if (caller_ws) plan = caller_plan(plan, ws, ws_bytes);
   GemmParams p{};
   p.A = (const uint16_t*)A;
   p.B = (const uint16_t*)B;
@@ -283,21 +356,42 @@ gemm_status_t run(int32_t dt, int64_t M, int64_t N, int64_t K, const void* A, in
   if (plan.kid == KID_GENERAL) {
     return launch_general(dt, p, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
   }
+  if (!tiled_has(plan.kid, dt)) return GEMM_ERR_NOT_SUPPORTED;
   std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);
   if (plan.workspace > 0) {
     void* w = nullptr;
     if (caller_ws) {
-      if (ws == nullptr || ws_bytes < plan.workspace || ((uintptr_t)ws & 255))
-        return GEMM_ERR_WORKSPACE;
+      if (!workspace_fits(plan, ws, ws_bytes)) return GEMM_ERR_WORKSPACE;
       w = ws;
     } else {
       ws_lock.lock();  // released once the kernels are enqueued
       st = library_workspace(dev, stream, plan.workspace, &w);
+      if (st == GEMM_ERR_ALLOC && (plan.pack_a || plan.pack_b)) {
+        // No room for the packed copies: the general kernel needs none.
+        ws_lock.unlock();
+        return launch_general(dt, p, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+      }
       if (st != GEMM_OK) return st;
     }
-    p.partials = (f32x4_storage*)w;
+    p.partials = (f32x4_storage*)w;  // partial tiles, when the schedule has any
+    // Packed operands follow the partial tiles: rows of kp elements, 16-byte
+    // aligned, zero past K. The tiled plan then runs over kp.
+    char* next = (char*)w + plan.partial_bytes;
+    if (plan.pack_a) {
+      if (launch_pack(p.A, lda, (int32_t)K, M, (int32_t)plan.kp, next, stream) != hipSuccess)
+        return GEMM_ERR_HIP;
+      p.A = (const uint16_t*)next;
+      p.lda = plan.kp;
+      next += round256(M * plan.kp * 2);
+    }
+    if (plan.pack_b) {
+      if (launch_pack(p.B, ldb, (int32_t)K, N, (int32_t)plan.kp, next, stream) != hipSuccess)
+        return GEMM_ERR_HIP;
+      p.B = (const uint16_t*)next;
+      p.ldb = plan.kp;
+    }
+    if (plan.pack_a || plan.pack_b) p.K = (int32_t)plan.kp;
   }
-  if (!tiled_has(plan.kid, dt)) return GEMM_ERR_NOT_SUPPORTED;
   return launch_tiled(plan.kid, dt, p, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
@@ -322,7 +416,10 @@ size_t gemm_f16_f32_abt_workspace_size(int64_t M, int64_t N, int64_t K) {
   const int64_t ld = K % 8 ? K + (8 - K % 8) : K;
   const Plan plan = make_plan(M, N, K, aligned, ld, aligned, ld, (const float*)aligned, N,
                               kDefaultCUs);
-  // The plan for other alignments never needs more than this many tiles.
+  // With K not a multiple of 8 the rows of both operands are packed (no row
+  // stride makes them 16-byte aligned), and this includes the copies. Other
+  // misaligned operands pack only into a caller workspace large enough for
+  // them; otherwise that call runs the general kernel.
   return plan.workspace;
 }
 
@@ -372,12 +469,16 @@ gemm_status_t gemm_f16_f32_abt_describe(int64_t M, int64_t N, int64_t K, char* b
   } else {
     const KernelInfo* ki = kernel_info(plan.kid);
     const Sched& s = plan.s;
+    char pack[64] = "";
+    if (plan.pack_a || plan.pack_b)
+      std::snprintf(pack, sizeof(pack), " pack=%s%s kp=%lld", plan.pack_a ? "A" : "",
+                    plan.pack_b ? "B" : "", (long long)plan.kp);
     std::snprintf(buf, len,
                   "M=%lld N=%lld K=%lld kernel=%s kid=%d mode=%s splits=%d tiles=%d (%dx%d) "
-                  "k_iters=%d grid=%d group_m=%d xcd_remap=%d slots=%d lds=%d workspace=%zu",
+                  "k_iters=%d grid=%d group_m=%d xcd_remap=%d slots=%d lds=%d workspace=%zu%s",
                   (long long)M, (long long)N, (long long)K, ki->name, plan.kid,
                   mode_name(s.mode), s.splits, s.tiles, s.tiles_m, s.tiles_n, s.k_iters, s.grid,
-                  s.group_m, s.xcd_remap, s.slots, ki->lds_bytes, plan.workspace);
+                  s.group_m, s.xcd_remap, s.slots, ki->lds_bytes, plan.workspace, pack);
   }
   return GEMM_OK;
 }

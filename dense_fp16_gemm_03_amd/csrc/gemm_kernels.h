@@ -103,6 +103,12 @@ bool tiled_has(int32_t kid, int32_t dt);
 // Launches the general kernel over ceil(M/64) x ceil(N/64) workgroups.
 hipError_t launch_general(int32_t dt, const GemmParams& p, hipStream_t stream);
 
+// Copies `rows` rows of K 16-bit elements (row i at src + i * ld, any 2-byte
+// alignment) to dst as rows of kp elements (kp = K rounded up to 8, dst
+// 16-byte aligned), zero-filling elements K .. kp - 1.
+hipError_t launch_pack(const uint16_t* src, int64_t ld, int32_t K, int64_t rows, int32_t kp,
+                       void* dst, hipStream_t stream);
+
 // Workgroups of kernel `kid` that fit on one CU at once (0 on error).
 int32_t tiled_occupancy(int32_t kid);
 

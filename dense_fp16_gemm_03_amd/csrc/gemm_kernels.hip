@@ -1004,6 +1004,31 @@ __global__ __launch_bounds__(256) void gemm_general_kernel(GemmParams p, int32_t
   }
 }
 
+// Operand packing: one thread per 16-byte chunk of the packed copy, taking
+// elements one by one from a source row of any 2-byte alignment and writing
+// the chunk with one 16-byte store; elements past K are zero, so they add
+// nothing to C. Workgroups walk the chunks by stride.
+__global__ __launch_bounds__(256) void pack_rows_kernel(const uint16_t* __restrict__ src,
+                                                        int64_t ld, int32_t K,
+                                                        int32_t chunks_per_row, int64_t chunks,
+                                                        u32x4* __restrict__ dst) {
+  const int64_t step = (int64_t)gridDim.x * 256;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < chunks; t += step) {
+    const int64_t r = t / chunks_per_row;
+    const int k0 = (int)(t - r * chunks_per_row) * 8;
+    const uint16_t* row = src + r * ld;
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = k0 + 2 * q;
+      const uint32_t lo = k < K ? row[k] : 0u;
+      const uint32_t hi = k + 1 < K ? row[k + 1] : 0u;
+      w[q] = lo | (hi << 16);
+    }
+    dst[t] = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
 #define G16_CFG(id, name, bm, bn, bk, st, wgm, wgn, mi, rs, pp) \
   using K##id = Cfg<bm, bn, bk, st, wgm, wgn, mi, rs, pp>;
 G16_TILED_KERNELS(G16_CFG)
@@ -1133,6 +1158,17 @@ hipError_t launch_general(int32_t dt, const GemmParams& p, hipStream_t stream) {
   else
     hipLaunchKernelGGL(gemm_general_kernel<DT_F16>, dim3(grid), dim3(256), 0, stream, p,
                        (int32_t)tiles_n, tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const uint16_t* src, int64_t ld, int32_t K, int64_t rows, int32_t kp,
+                       void* dst, hipStream_t stream) {
+  const int32_t per_row = kp / 8;
+  const int64_t chunks = rows * per_row;
+  if (chunks <= 0) return hipSuccess;
+  const uint32_t grid = (uint32_t)min_of<int64_t>((chunks + 255) / 256, (int64_t)1 << 20);
+  hipLaunchKernelGGL(pack_rows_kernel, dim3(grid), dim3(256), 0, stream, src, ld, K, per_row,
+                     chunks, (u32x4*)dst);
   return hipGetLastError();
 }
 

@@ -47,8 +47,11 @@ typedef enum {
  * M, N and K above 2147482623 (2^31 - 1025; the kernels index in 32 bits)
  * return GEMM_ERR_NOT_SUPPORTED; strides and byte sizes may exceed 2^31.
  * Any alignment of pointers and strides is accepted: 16-byte aligned A, B
- * with lda, ldb, K multiples of 8 take the tiled MFMA kernels, anything else
- * a slower general kernel. Split-K / stream-K plans write fp32 partial tiles
+ * with lda, ldb, K multiples of 8 take the tiled MFMA kernels directly. When
+ * an operand breaks these rules and M*N*K >= 2^22, a pack kernel first copies
+ * it into the workspace as rows of K rounded up to 8 elements (zero past K)
+ * and the tiled kernels run on the copy; smaller products take a slower
+ * general kernel. Split-K / stream-K plans write fp32 partial tiles
  * to a workspace and a second kernel on the same stream sums them, in a fixed
  * (k) order, into C, so results do not depend on timing. The workspace is
  * library-owned, allocated once per (device, stream) on first use and grown
@@ -60,13 +63,17 @@ gemm_status_t gemm_f16_f32_abt(int64_t M, int64_t N, int64_t K,
                                const void* B, int64_t ldb,
                                float* C, int64_t ldc, void* stream);
 
-/* Bytes of workspace gemm_f16_f32_abt_ws needs for this shape (0 if none). */
+/* Bytes of workspace gemm_f16_f32_abt_ws needs for this shape (0 if none),
+ * for 16-byte aligned operands with row strides a multiple of 8; when K is
+ * not a multiple of 8 it includes the packed copies of both operands. */
 size_t gemm_f16_f32_abt_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /* As gemm_f16_f32_abt, with a caller-owned device workspace of at least
  * gemm_f16_f32_abt_workspace_size(M, N, K) bytes, 256-byte aligned. Its
  * contents on entry do not matter. Two calls in flight at once must not share
- * it. workspace may be NULL when the size is 0. */
+ * it. workspace may be NULL when the size is 0. Operands that would be packed
+ * are packed only if the workspace also holds their copies; otherwise the
+ * call runs the general kernel (never an error for that reason). */
 gemm_status_t gemm_f16_f32_abt_ws(int64_t M, int64_t N, int64_t K,
                                   const void* A, int64_t lda,
                                   const void* B, int64_t ldb,

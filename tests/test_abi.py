@@ -118,6 +118,24 @@ def test_describe_size_limit(lib):
             gemm.gemm_f16_f32_abt_describe(M, N, K)
 
 
+def test_packed_plans(lib, monkeypatch):
+    """K % 8 != 0 on a large enough product: both operands are packed into
+    rows of K rounded up to 8, and the workspace size counts the copies."""
+    M, N, K = 1024, 1024, 1001
+    text = gemm.gemm_f16_f32_abt_describe(M, N, K)
+    assert "pack=AB kp=1008" in text and "kernel=64x64x64" in text
+    assert gemm.gemm_f16_f32_abt_workspace_size(M, N, K) == 2 * (M * 1008 * 2)
+    M, N, K = 2048, 2048, 4095  # packed, and a split plan: partial tiles first
+    text = gemm.gemm_f16_f32_abt_describe(M, N, K)
+    assert "pack=AB kp=4096" in text and "mode=split" in text
+    parts = 64 * 2 * 256 * 256 * 4
+    assert gemm.gemm_f16_f32_abt_workspace_size(M, N, K) == parts + 2 * (M * 4096 * 2)
+    assert "pack" not in gemm.gemm_f16_f32_abt_describe(2048, 2048, 4096)
+    monkeypatch.setenv("GEMM_F16_PLAN", "general=1")
+    assert "general" in gemm.gemm_f16_f32_abt_describe(1024, 1024, 1001)
+    assert gemm.gemm_f16_f32_abt_workspace_size(1024, 1024, 1001) == 0
+
+
 def test_describe_general_and_empty(lib):
     assert "general" in gemm.gemm_f16_f32_abt_describe(100, 100, 13)  # K % 8 != 0
     assert "nothing" in gemm.gemm_f16_f32_abt_describe(0, 100, 13)

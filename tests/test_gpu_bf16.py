@@ -145,6 +145,22 @@ def test_general_kernel_odd_k_and_unaligned_views():
           run(At, Bt), "uniform", "unaligned strided views")
 
 
+@pytest.mark.parametrize("M,N,K", [(1024, 1024, 1001), (600, 520, 1355)])
+def test_packed_operands(M, N, K):
+    """K % 8 != 0 on a product large enough to pack both operands into
+    aligned, zero-padded copies before the tiled kernel."""
+    assert "pack=AB" in gemm.gemm_f16_f32_abt_describe(M, N, K)
+    A, B = inputs.integer_bf16(M, K, 175), inputs.integer_bf16(N, K, 176)
+    check(A, B, run(A, B), "integer", f"packed {M}x{N}x{K} integer")
+    A, B = inputs.uniform_bf16(M, K, 177), inputs.uniform_bf16(N, K, 178)
+    check(A, B, run(A, B), "uniform", f"packed {M}x{N}x{K} uniform")
+    # K % 8 == 0 with A one element off a 16-byte boundary: A alone is packed
+    big_a = inputs.integer_bf16(M, 1025, 179)
+    B = inputs.integer_bf16(N, 1024, 180)
+    check(np.ascontiguousarray(big_a[:, 1:]), B, run(to_dev(big_a)[:, 1:], to_dev(B)),
+          "integer", "packed misaligned A")
+
+
 def test_k_zero_writes_zeros():
     A = torch.empty((40, 0), dtype=torch.bfloat16, device=DEV)
     B = torch.empty((30, 0), dtype=torch.bfloat16, device=DEV)

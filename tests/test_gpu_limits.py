@@ -1,14 +1,15 @@
 """The largest sizes (needs an MI355X).
 
 * C and A beyond 2 GiB and 4 GiB (64-bit row offsets in every kernel's
-  loads and stores), on the default plan, two forced tiled kernels and the
-  general kernel;
+  loads and stores), on the default plan, two forced tiled kernels, a
+  misaligned B packed into aligned rows, and the general kernel;
 * 65792 output tiles, 257 per workgroup of the persistent grid, with a 17 GB C;
 * K = 2^20 on one tile: 256 k-shares, the most the split rule makes;
 * row strides on both sides of the 2^31-byte buffer-offset limit of the
   tiled kernels (padding columns hold NaN, so a read past K shows);
-* M at the library's 32-bit index limit (2^31 - 1025), on the tiled path and
-  on the general kernel, whose grid then walks 33.5 million tiles by stride.
+* M at the library's 32-bit index limit (2^31 - 1025), on the tiled path
+  (B direct or packed) and on the general kernel, whose grid then walks 33.5
+  million tiles by stride.
 
 Operands of gigabytes are drawn on the GPU (inputs.device_uniform) and the
 rows a check needs are copied back for the CPU reference. Every C starts as
@@ -46,10 +47,20 @@ def _each(request, monkeypatch):
     torch.cuda.empty_cache()
 
 
-def plan_text(M, N, K, misaligned_b):
-    if misaligned_b:  # the plan rule sends operands off 16-byte alignment there
-        return "general kernel (B not 16-byte aligned)"
+def plan_text(M, N, K, path):
+    if path == "general":
+        return "general kernel (forced; B not 16-byte aligned)"
+    if path == "packed":  # describe() sees no pointers: B is packed, then this plan
+        return "B packed into aligned rows, then " + gemm.gemm_f16_f32_abt_describe(M, N, K)
     return gemm.gemm_f16_f32_abt_describe(M, N, K)
+
+
+def misaligned(B_host):
+    """B on the GPU one element past a 16-byte boundary (row stride K + 8)."""
+    N, K = B_host.shape
+    buf = torch.zeros((N, K + 8), dtype=torch.float16, device=DEV)
+    buf[:, 1:K + 1] = torch.from_numpy(B_host).to(DEV)
+    return buf[:, 1:K + 1]
 
 
 def nan_c(M, N):
@@ -97,21 +108,20 @@ def sample_rows(M, extra, n_rand, seed):
     return sorted(r for r in rows if 0 <= r < M)
 
 
-@pytest.mark.parametrize("plan", ["default", "kid=16", "kid=18", "general"])
+@pytest.mark.parametrize("plan", ["default", "kid=16", "kid=18", "packed", "general"])
 def test_tall_c_beyond_2gib(plan, monkeypatch):
     M, N, K = (1 << 21) + 37, 264, 1032  # A 4.3 GB, C 2.2 GB; N and M ragged
     A = inputs.device_uniform(M, K, 501, DEV)
     B_host = inputs.uniform(N, K, 502)
-    if plan == "general":
-        # B one element past a 16-byte boundary: only the general kernel takes it
-        B_buf = torch.zeros((N, K + 8), dtype=torch.float16, device=DEV)
-        B_buf[:, 1:K + 1] = torch.from_numpy(B_host).to(DEV)
-        B = B_buf[:, 1:K + 1]
+    if plan in ("packed", "general"):
+        B = misaligned(B_host)  # packed into aligned rows, or the general kernel
+        if plan == "general":
+            monkeypatch.setenv("GEMM_F16_PLAN", "general=1")
     else:
         B = torch.from_numpy(B_host).to(DEV)
         if plan != "default":
             monkeypatch.setenv("GEMM_F16_PLAN", plan)
-    log(f"  plan: {plan_text(M, N, K, plan == 'general')} ({plan})")
+    log(f"  plan: {plan_text(M, N, K, plan)} ({plan})")
     C = nan_c(M, N)
     gemm.gemm_abt(A, B, C)
     torch.cuda.synchronize()
@@ -165,12 +175,16 @@ def test_most_k_shares():
     assert ok.all(), f"{(~ok).sum()} elements outside 1e-5*S"
 
 
-def test_row_stride_at_offset_limit():
+def test_row_stride_at_offset_limit(monkeypatch):
     # The tiled kernels address a 256-row operand tile with 32-bit byte
-    # offsets: (256 - 1) * ld * 2 + (K + 32) * 2 must stay below 2^31.
+    # offsets: (256 - 1) * ld * 2 + (K + 32) * 2 must stay below 2^31. One
+    # stride step further the operands are packed into rows of K elements
+    # (or, forced, run on the general kernel).
     M, N, K = 256, 256, 4096
     ld_in = ((2**31 - 1 - (K + 32) * 2) // (255 * 2)) // 8 * 8
-    for ld, expect in ((ld_in, "tiled"), (ld_in + 8, "general")):
+    for ld, expect in ((ld_in, "tiled"), (ld_in + 8, "packed"), (ld_in + 8, "general")):
+        if expect == "general":
+            monkeypatch.setenv("GEMM_F16_PLAN", "general=1")
         A = inputs.device_uniform(M, K, 531, DEV, ld=ld)
         B = inputs.device_uniform(N, K, 532, DEV, ld=ld)
         log(f"  ld={ld} ({expect}; A and B {2 * M * ld / 2**30:.2f} GiB each)")
@@ -187,18 +201,18 @@ def test_row_stride_at_offset_limit():
         torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("path", ["tiled", "general"])
-def test_m_at_index_limit(path):
+@pytest.mark.parametrize("path", ["tiled", "packed", "general"])
+def test_m_at_index_limit(path, monkeypatch):
     M, N, K = MAX_DIM, 1, 8  # A 34.4 GB, C 8.6 GB
     A = inputs.device_uniform(M, K, 541, DEV)
     B_host = inputs.uniform(N, K, 542)
-    if path == "general":
-        B_buf = torch.zeros((N, K + 8), dtype=torch.float16, device=DEV)
-        B_buf[:, 1:K + 1] = torch.from_numpy(B_host).to(DEV)
-        B = B_buf[:, 1:K + 1]
+    if path in ("packed", "general"):
+        B = misaligned(B_host)
+        if path == "general":
+            monkeypatch.setenv("GEMM_F16_PLAN", "general=1")
     else:
         B = torch.from_numpy(B_host).to(DEV)
-    log(f"  plan: {plan_text(M, N, K, path == 'general')} ({path})")
+    log(f"  plan: {plan_text(M, N, K, path)} ({path})")
     C = nan_c(M, N)
     gemm.gemm_abt(A, B, C)
     torch.cuda.synchronize()

@@ -204,8 +204,13 @@ def test_ragged_shapes(M, N, K):
     assert_exact(run(Ai, Bi), ref, f"{M}x{N}x{K} integer")
 
 
-@pytest.mark.parametrize("M,N,K", [(100, 90, 13), (64, 64, 7), (300, 200, 1001), (5, 3, 1)])
-def test_general_kernel_odd_k(M, N, K):
+@pytest.mark.parametrize("M,N,K,force", [(100, 90, 13, False), (64, 64, 7, False),
+                                         (5, 3, 1, False), (300, 200, 1001, True)])
+def test_general_kernel_odd_k(M, N, K, force, monkeypatch):
+    """The general kernel: small products with K % 8 != 0 take it by the plan
+    rule; a larger one is forced onto it (it would otherwise be packed)."""
+    if force:
+        monkeypatch.setenv("GEMM_F16_PLAN", "general=1")
     assert "general" in gemm.gemm_f16_f32_abt_describe(M, N, K)
     A = inputs.uniform(M, K, 111)
     B = inputs.uniform(N, K, 112)
@@ -213,15 +218,21 @@ def test_general_kernel_odd_k(M, N, K):
     assert_tol(run(A, B), ref, S, f"general {M}x{N}x{K}")
 
 
-def test_strided_and_unaligned_views():
+@pytest.mark.parametrize("plan", ["", "general=1"])
+def test_strided_and_unaligned_views(plan, monkeypatch):
+    """Views with row strides past K and pointers off 16 bytes: (1, 3) is
+    packed into aligned copies by default and run on the general kernel when
+    forced."""
+    if plan:
+        monkeypatch.setenv("GEMM_F16_PLAN", plan)
     M, N, K = 300, 200, 256
     Abig = to_dev(inputs.integer(M, K + 24, 121))
     Bbig = to_dev(inputs.integer(N, K + 40, 122))
-    for a0, b0 in ((0, 0), (8, 16), (1, 3)):  # (1, 3): not 16-byte aligned -> general kernel
+    for a0, b0 in ((0, 0), (8, 16), (1, 3)):
         a = Abig[:, a0:a0 + K]
         b = Bbig[:, b0:b0 + K]
         ref, _ = oracle.gemm_abt(a.cpu().numpy(), b.cpu().numpy())
-        assert_exact(run(a, b), ref, f"views offset {a0},{b0}")
+        assert_exact(run(a, b), ref, f"views offset {a0},{b0} {plan}")
     # C with a row stride larger than N
     Cbig = torch.full((M, N + 12), np.nan, dtype=torch.float32, device=DEV)
     c = Cbig[:, 4:4 + N]
@@ -231,6 +242,48 @@ def test_strided_and_unaligned_views():
     out = Cbig.cpu().numpy()
     assert_exact(out[:, 4:4 + N], ref, "strided C")
     assert np.isnan(out[:, :4]).all() and np.isnan(out[:, 4 + N:]).all(), "wrote outside C"
+
+
+# Operands the tiled kernels cannot load directly, large enough to be packed
+# into aligned, zero-padded copies first: K % 8 != 0 (both operands), and a
+# pointer one element past a 16-byte boundary with K % 8 == 0 (that operand).
+PACKED = [(300, 200, 1001, 0), (1024, 1024, 1001, 0), (777, 555, 4095, 0),
+          (2048, 2048, 4095, 0), (1024, 768, 1024, 1)]
+
+
+@pytest.mark.parametrize("M,N,K,a_off", PACKED)
+def test_packed_operands(M, N, K, a_off):
+    if K % 8:
+        assert "pack=AB" in gemm.gemm_f16_f32_abt_describe(M, N, K)
+    Ai = inputs.integer(M, K + a_off, 141)
+    Bi = inputs.integer(N, K, 142)
+    a = to_dev(Ai)[:, a_off:a_off + K]
+    A = np.ascontiguousarray(Ai[:, a_off:])
+    ref, _ = oracle.gemm_abt(A, Bi)
+    assert_exact(run(a, to_dev(Bi)), ref, f"packed {M}x{N}x{K} integer")
+    Au = inputs.uniform(M, K + a_off, 143)
+    Bu = inputs.uniform(N, K, 144)
+    A = np.ascontiguousarray(Au[:, a_off:])
+    rows, cols = sample_points(M, N, n_rand=2000, seed=5)
+    ref, S = oracle.gemm_abt_elems(A, Bu, rows, cols)
+    got = run(to_dev(Au)[:, a_off:a_off + K], to_dev(Bu))[rows, cols]
+    assert_tol(got, ref, S, f"packed {M}x{N}x{K} uniform (sampled)")
+
+
+def test_packed_caller_workspace():
+    """With K % 8 != 0 the caller workspace size includes the packed copies and
+    the _ws call packs; with no workspace it runs the general kernel instead.
+    Integer inputs: both paths equal the reference bit for bit."""
+    M, N, K = 1024, 1024, 1001
+    Ai, Bi = inputs.integer(M, K, 145), inputs.integer(N, K, 146)
+    ref, _ = oracle.gemm_abt(Ai, Bi)
+    need = gemm.gemm_f16_f32_abt_workspace_size(M, N, K)
+    assert need >= 2 * (M + N) * 1008 // 2  # both packed copies (kp = 1008)
+    At, Bt = to_dev(Ai), to_dev(Bi)
+    ws = torch.full((need,), 255, dtype=torch.uint8, device=DEV)
+    assert_exact(run(At, Bt, workspace=ws), ref, "packed into the caller workspace")
+    small = torch.empty((256,), dtype=torch.uint8, device=DEV)
+    assert_exact(run(At, Bt, workspace=small), ref, "general kernel (workspace too small)")
 
 
 def test_k_zero_writes_zeros():
@@ -433,12 +486,15 @@ def test_threads_share_a_stream():
             assert np.array_equal(C.cpu().numpy(), refs[i]), f"shape {shapes[i]}"
 
 
-@pytest.mark.parametrize("name", ["1024^3", "4096x4096x1024", "2048x2048x16384"])
+@pytest.mark.parametrize("name", ["1024^3", "4096x4096x1024", "2048x2048x16384",
+                                  "1024x1024x1001"])
 def test_graph_replay(name):
     """A call captured in a HIP graph (torch.cuda.CUDAGraph) replays to the eager
     result, bitwise, on every replay, with eager work between replays. Split
-    plans use a caller workspace, allocated before capture."""
-    M, N, K = WORKLOADS.get(name) or inputs.PAGE_SHAPES[name]
+    plans and packed operands (K % 8 != 0) use a caller workspace, allocated
+    before capture."""
+    M, N, K = (WORKLOADS.get(name) or inputs.PAGE_SHAPES.get(name)
+               or tuple(int(v) for v in name.split("x")))
     A, B = operands((M, N, K), "uniform")
     At, Bt = to_dev(A), to_dev(B)
     eager = run(At, Bt)

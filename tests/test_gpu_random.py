@@ -8,8 +8,10 @@ fp32, so C must equal the CPU reference bit for bit whatever the summation
 order. C sits inside a NaN-filled buffer with padding columns on both sides:
 after the call the padding must still be NaN (no store outside C).
 
-About a quarter of the cases use unaligned pointers or strides, which the
-plan rule sends to the general kernel; the rest take the forced tiled kernel.
+About a quarter of the cases use unaligned pointers or strides (or K not a
+multiple of 8): the plan rule packs those operands into aligned copies when
+the product is large enough, else runs the general kernel; about one case in
+ten forces the general kernel.
 """
 import numpy as np
 import pytest
@@ -55,6 +57,8 @@ def draw(i):
         plan += ",mode=2"
     if rng.random() < 0.5:
         plan += f",grid={int(rng.integers(1, 300))}"
+    if rng.random() < 0.1:
+        plan = "general=1"
     return dict(M=M, N=N, K=K, pad_a=pad_a, pad_b=pad_b, off_a=off_a, off_b=off_b,
                 pad_c=pad_c, off_c=off_c, dtype=dtype, plan=plan)
 
