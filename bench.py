@@ -304,6 +304,14 @@ def library_md5() -> str:
         return hashlib.md5(f.read()).hexdigest()
 
 
+def parse_shape(text):
+    """(M, N, K) from 'MxNxK' with positive integers, else None."""
+    parts = text.split("x")
+    if len(parts) != 3 or not all(p.isdigit() and int(p) > 0 for p in parts):
+        return None
+    return tuple(int(p) for p in parts)
+
+
 def traffic_for(workload, kernel_avg_s):
     """HBM bytes per launch from committed rocprofv3 counters, if they match this source."""
     try:
@@ -325,7 +333,8 @@ def main():
     ap.add_argument("--dtype", default="f16", choices=("f16", "bf16"),
                     help="operand type: binary16 (the workloads' type) or bfloat16")
     ap.add_argument("--workload", default="8192^3",
-                    help="one of the five workloads, or one of the pages' other shapes")
+                    help="one of the five workloads, one of the pages' other shapes, "
+                         "or any MxNxK")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-telemetry", action="store_true",
                     help="skip the amd-smi clock/power sample after the timed region")
@@ -363,10 +372,12 @@ def main():
 
     name = args.workload
     all_shapes = {**inputs.WORKLOADS, **inputs.PAGE_SHAPES}
-    if name not in all_shapes:
-        print(f"unknown workload {name!r}; known: {', '.join(all_shapes)}", file=sys.stderr)
+    shape = all_shapes.get(name) or parse_shape(name)
+    if shape is None:
+        print(f"unknown workload {name!r}; known: {', '.join(all_shapes)}, or MxNxK",
+              file=sys.stderr)
         sys.exit(2)
-    M, N, K = all_shapes[name]
+    M, N, K = shape
     flops, nbytes = algorithmic(M, N, K)
     log(f"[bench] workload {name}: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
     A, B, At, Bt = make_device_operands(torch, (M, N, K), dev, args.dtype)

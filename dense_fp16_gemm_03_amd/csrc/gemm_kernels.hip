@@ -1004,10 +1004,15 @@ __global__ __launch_bounds__(256) void gemm_general_kernel(GemmParams p, int32_t
   }
 }
 
-// Operand packing: one thread per 16-byte chunk of the packed copy, taking
-// elements one by one from a source row of any 2-byte alignment and writing
-// the chunk with one 16-byte store; elements past K are zero, so they add
-// nothing to C. Workgroups walk the chunks by stride.
+// Operand packing: one thread per 16-byte chunk (8 elements) of the packed
+// copy. The chunk's source bytes start at any 2-byte boundary, so the thread
+// loads the aligned 16-byte block holding its first element and, when a valid
+// element lies past it, the next block; it shifts the 8 elements into place
+// (v_alignbyte) and zeroes those at or past K. Neighbouring lanes load
+// neighbouring blocks, so the loads coalesce. A block is loaded only if it
+// holds a valid element of the row; an aligned 16-byte block never crosses a
+// page, so the bytes read beside the valid ones are always mapped (their
+// values are discarded). Workgroups walk the chunks by stride.
 __global__ __launch_bounds__(256) void pack_rows_kernel(const uint16_t* __restrict__ src,
                                                         int64_t ld, int32_t K,
                                                         int32_t chunks_per_row, int64_t chunks,
@@ -1016,16 +1021,28 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const uint16_t* __restri
   for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < chunks; t += step) {
     const int64_t r = t / chunks_per_row;
     const int k0 = (int)(t - r * chunks_per_row) * 8;
-    const uint16_t* row = src + r * ld;
-    uint32_t w[4];
+    const int nvalid = min_of(8, K - k0);  // >= 1: chunks stop at K rounded up to 8
+    const uint16_t* first = src + r * ld + k0;
+    const int s = (int)((uintptr_t)first & 15);  // byte offset in its block (even)
+    const u32x4* blk = (const u32x4*)((const char*)first - s);
+    const u32x4 b0 = blk[0];
+    const u32x4 b1 = s + 2 * nvalid > 16 ? blk[1] : u32x4{0u, 0u, 0u, 0u};
+    const uint32_t w[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+    const int q = s >> 2;  // first dword of the chunk in w
+    uint32_t d[5];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int k = k0 + 2 * q;
-      const uint32_t lo = k < K ? row[k] : 0u;
-      const uint32_t hi = k + 1 < K ? row[k + 1] : 0u;
-      w[q] = lo | (hi << 16);
+    for (int k = 0; k < 5; ++k)
+      d[k] = q == 0 ? w[k] : q == 1 ? w[k + 1] : q == 2 ? w[k + 2] : w[k + 3];
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[i] = (s & 2) ? __builtin_amdgcn_alignbyte(d[i + 1], d[i], 2) : d[i];
+      if (2 * i >= nvalid)
+        o[i] = 0u;
+      else if (2 * i + 1 >= nvalid)
+        o[i] &= 0xffffu;
     }
-    dst[t] = u32x4{w[0], w[1], w[2], w[3]};
+    dst[t] = u32x4{o[0], o[1], o[2], o[3]};
   }
 }
 

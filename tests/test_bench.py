@@ -21,6 +21,12 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in (r.stdout + r.stderr)
 
 
+def test_shape_parsing():
+    assert bench.parse_shape("4096x4096x1001") == (4096, 4096, 1001)
+    for bad in ("8192^3", "4096x4096", "0x5x5", "axbxc", "1x2x-3"):
+        assert bench.parse_shape(bad) is None
+
+
 def test_algorithmic_figures():
     flops, nbytes = bench.algorithmic(8192, 8192, 8192)
     assert flops == 2.0 * 8192**3
