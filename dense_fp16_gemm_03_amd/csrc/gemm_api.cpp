@@ -57,6 +57,12 @@ size_t span_bytes(int64_t rows, int64_t ld, int64_t cols, size_t elem) {
   return (size_t)((rows - 1) * ld + cols) * elem;
 }
 
+// A row stride whose operand would span 2^60 bytes or more (far beyond any
+// device's address space) is refused, so spans and offsets never overflow.
+bool stride_fits(int64_t rows, int64_t ld, int64_t elem) {
+  return rows <= 1 || ld <= ((int64_t)1 << 60) / (rows * elem);
+}
+
 gemm_status_t validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                        const void* B, int64_t ldb, const float* C, int64_t ldc) {
   if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_VALUE;
@@ -64,18 +70,22 @@ gemm_status_t validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t l
   if (M == 0 || N == 0) return GEMM_OK;
   if (C == nullptr) return GEMM_ERR_INVALID_VALUE;
   if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_INVALID_VALUE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_ERR_NOT_SUPPORTED;
+  if (!stride_fits(M, lda, 2) || !stride_fits(N, ldb, 2) || !stride_fits(M, ldc, 4))
+    return GEMM_ERR_NOT_SUPPORTED;
   const size_t cbytes = span_bytes(M, ldc, N, 4);
   if (K > 0 && (ranges_overlap(C, cbytes, A, span_bytes(M, lda, K, 2)) ||
                 ranges_overlap(C, cbytes, B, span_bytes(N, ldb, K, 2))))
     return GEMM_ERR_INVALID_VALUE;
-  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_ERR_NOT_SUPPORTED;
   if (((uintptr_t)A & 1) || ((uintptr_t)B & 1) || ((uintptr_t)C & 3))
     return GEMM_ERR_NOT_SUPPORTED;
   return GEMM_OK;
 }
 
-// Optional plan override for experiments: GEMM_F16_PLAN="kid=0,mode=1,splits=16,grid=256,group=4"
-// (any subset of keys). Read on every plan; unknown keys are ignored.
+// Optional plan override for experiments and tests:
+// GEMM_F16_PLAN="kid=0,mode=1,splits=16,grid=256,group=4,xcd=0" (any subset of
+// keys), or "general=1" for the general kernel. Read on every plan; unknown
+// keys are ignored.
 struct Override {
   int32_t kid = -1, mode = -1, splits = -1, grid = -1, group = -1, xcd = -1;
   int32_t general = 0;  // 1: the general kernel, whatever the operands

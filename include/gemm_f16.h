@@ -45,7 +45,8 @@ typedef enum {
  * Requirements: M, N, K >= 0; lda >= K; ldb >= K; ldc >= N; A, B, C non-NULL
  * when M*N > 0 (A, B may be NULL when K = 0); C must not overlap A or B.
  * M, N and K above 2147482623 (2^31 - 1025; the kernels index in 32 bits)
- * return GEMM_ERR_NOT_SUPPORTED; strides and byte sizes may exceed 2^31.
+ * return GEMM_ERR_NOT_SUPPORTED, as do strides that would make an operand
+ * span 2^60 bytes or more; strides and byte sizes may otherwise exceed 2^31.
  * Any alignment of pointers and strides is accepted: 16-byte aligned A, B
  * with lda, ldb, K multiples of 8 take the tiled MFMA kernels directly. When
  * an operand breaks these rules and M*N*K >= 2^22, a pack kernel first copies

@@ -61,6 +61,8 @@ MAX_DIM = (1 << 31) - 1025  # largest M, N or K the library takes
     ((MAX_DIM + 1, 4, 8, A_PTR, 8, B_PTR, 8, 1 << 44, 4), 2),  # M one past the limit
     ((4, MAX_DIM + 1, 8, A_PTR, 8, B_PTR, 8, 1 << 44, MAX_DIM + 1), 2),  # N past it
     ((4, 4, MAX_DIM + 1, A_PTR, MAX_DIM + 1, 1 << 40, MAX_DIM + 1, 1 << 44, 4), 2),  # K
+    ((4, 4, 8, A_PTR, 1 << 62, B_PTR, 8, 1 << 44, 4), 2),   # lda: span past 2^60 bytes
+    ((4, 4, 8, A_PTR, 8, B_PTR, 8, 1 << 44, 1 << 61), 2),   # ldc: span past 2^60 bytes
     ((0, 4, 8, A_PTR, 8, B_PTR, 8, C_PTR, 4), 0),           # M = 0: nothing to do
     ((4, 0, 8, 0, 8, 0, 8, 0, 0), 0),                       # N = 0: nothing to do
 ])
