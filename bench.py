@@ -2,7 +2,7 @@
 """Benchmark of C = A * B^T (fp16 in, fp32 accumulate/out) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8192^3] [--dtype f16|bf16]
-                    [--no-cpu-baseline] [--shapes] [--vendor] [--calibrate-copy]
+                    [--no-cpu-baseline] [--no-long-k] [--shapes] [--vendor] [--calibrate-copy]
 
 A step is one call of gemm_f16_f32_abt through the C ABI on synthetic
 operands already resident in HBM (uniform [-1, 1] fp16, seeds 1 and 2). The
@@ -11,6 +11,13 @@ timed region is K back-to-back calls bracketed by device synchronisation;
 events on the launch stream: their mean is the kernel's average launch
 duration, from which `roofline.achieved` is computed against the fp16 MFMA
 peak (2.5 PFLOP/s dense).
+
+At 8192^3 the line also carries `long_k`: the two long-K workloads, 200
+back-to-back calls after 100 untimed ones, between one pair of HIP events
+(their main and reduce kernels and the gaps between calls), as fractions of
+peak beside the headline; `--no-long-k` leaves them out. The default 30
+warm-up calls of the headline, and the 100 here, let the board's clocks
+settle: the first 20 or so calls of a new shape run several percent slower.
 
 With --shapes, per-shape lines (`shapes`) time the five workloads the way "SASS-Level Kernel
 Generation for Blackwell" measures (section "How we measured"): every call
@@ -104,6 +111,22 @@ def time_throughput(torch, gemm, At, Bt, C, steps, warmup):
     t1 = time.perf_counter()
     kernel_ms = [s.elapsed_time(e) for s, e in ev]
     return t1 - t0, kernel_ms
+
+
+def time_loop(torch, gemm, At, Bt, C, calls, warmup):
+    """Microseconds per call over `calls` back-to-back calls, from one pair of
+    HIP events around the whole loop (no event between calls)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        gemm.gemm_abt(At, Bt, C, stream=stream)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record(stream)
+    for _ in range(calls):
+        gemm.gemm_abt(At, Bt, C, stream=stream)
+    e.record(stream)
+    e.synchronize()
+    return s.elapsed_time(e) * 1e3 / calls
 
 
 def time_calls_alone(torch, gemm, At, Bt, C, calls, warmup=20):
@@ -329,13 +352,16 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--dtype", default="f16", choices=("f16", "bf16"),
                     help="operand type: binary16 (the workloads' type) or bfloat16")
     ap.add_argument("--workload", default="8192^3",
                     help="one of the five workloads, one of the pages' other shapes, "
                          "or any MxNxK")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long-k", action="store_true",
+                    help="at 8192^3, skip the back-to-back timing of the two long-K workloads "
+                         "(profiling runs use this so their traces hold one shape)")
     ap.add_argument("--no-telemetry", action="store_true",
                     help="skip the amd-smi clock/power sample after the timed region")
     ap.add_argument("--shapes", action="store_true",
@@ -436,6 +462,26 @@ def main():
                 entry["pages_b200_us"] = PAGE_US[n]
             shapes.append(entry)
 
+    long_k = []
+    if name == "8192^3" and not args.no_long_k:
+        # The two long-K workloads, back to back like the headline, so every
+        # bench line carries their fraction of peak as well (not the value).
+        for n in ("2048x2048x16384", "1024x1024x65536"):
+            m, nn, k = inputs.WORKLOADS[n]
+            _, _, a, b = make_device_operands(torch, (m, nn, k), dev, args.dtype)
+            c = torch.empty((m, nn), dtype=torch.float32, device=dev)
+            # the board's clocks settle over the first ~100 calls of a new shape
+            avg_us = time_loop(torch, gemm, a, b, c, 200, 100)
+            f, _ = algorithmic(m, nn, k)
+            long_k.append({"workload": n, "us_per_call": round(avg_us, 3),
+                           "tflops": round(f / (avg_us * 1e-6) / 1e12, 2),
+                           "mfma_peak_frac": round(f / (avg_us * 1e-6) / 1e12 / PEAK_TFLOPS, 4),
+                           "calls": 200, "plan": gemm.gemm_f16_f32_abt_describe(m, nn, k)})
+            log(f"[bench] {n}: {avg_us:.2f} us/call back to back "
+                f"({long_k[-1]['mfma_peak_frac'] * 100:.1f}% of peak)")
+            del a, b, c
+            torch.cuda.empty_cache()
+
     vendor = None
     if args.vendor:
         vendor = vendor_arm(torch, gemm, list(inputs.WORKLOADS), dev)
@@ -463,7 +509,8 @@ def main():
                    "accumulate": "f32", "output": "f32",
                    "plan": gemm.gemm_f16_f32_abt_describe(M, N, K),
                    "source_hash": source_hash(), "library_md5": library_md5()},
-        "roofline": roofline, "cpu_baseline": cpu, "shapes": shapes, "telemetry": tele,
+        "roofline": roofline, "cpu_baseline": cpu, "shapes": shapes, "long_k": long_k,
+        "telemetry": tele,
     }
     if vendor is not None:
         line["vendor_hipblaslt"] = vendor
