@@ -97,7 +97,8 @@ Override read_override() {
   if (!env) return o;
   char buf[256];
   std::snprintf(buf, sizeof(buf), "%s", env);
-  for (char* tok = std::strtok(buf, ","); tok; tok = std::strtok(nullptr, ",")) {
+  char* save = nullptr;  // strtok_r: calls may plan on several host threads at once
+  for (char* tok = strtok_r(buf, ",", &save); tok; tok = strtok_r(nullptr, ",", &save)) {
     char key[32];
     int val = 0;
     if (std::sscanf(tok, "%31[^=]=%d", key, &val) != 2) continue;

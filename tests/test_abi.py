@@ -233,3 +233,28 @@ def test_default_plans(lib):
     for M, N, K in inputs.WORKLOADS.values():
         rows, _, _ = gemm.gemm_f16_schedule_dump(M, N, K)
         assert rows[:, 0].max() < 256
+
+
+def test_plan_override_parsed_on_many_threads(lib, monkeypatch):
+    """The override is parsed on every plan; ctypes releases the GIL, so
+    these calls run concurrently and every one must see the same plan."""
+    import threading
+
+    monkeypatch.setenv("GEMM_F16_PLAN", "kid=16,mode=1,splits=3,grid=40,group=2")
+    want = gemm.gemm_f16_f32_abt_describe(600, 520, 1352)
+    assert "kid=16" in want and "splits=3" in want and "grid=40" in want
+    bad = []
+
+    def worker():
+        for _ in range(2000):
+            got = gemm.gemm_f16_f32_abt_describe(600, 520, 1352)
+            if got != want:
+                bad.append(got)
+                return
+
+    threads = [threading.Thread(target=worker) for _ in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad, bad[:2]
