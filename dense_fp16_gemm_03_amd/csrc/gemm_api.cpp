@@ -13,6 +13,7 @@
 #include <utility>
 
 #include "gemm_kernels.h"
+#include "gemm_lds_layout.h"
 
 namespace {
 
@@ -507,6 +508,16 @@ void gemm_f16_release_workspaces(void) {
       ++it;
     }
   }
+}
+
+int32_t gemm_f16_lds_chunk(int32_t chunks_per_row, int32_t block_dim, int32_t row,
+                           int32_t chunk) {
+  if (row < 0 || chunk < 0 || chunk >= chunks_per_row) return -1;
+  if (chunks_per_row == 8 && block_dim == 32) return swz<8, 32>(row, chunk);
+  if (chunks_per_row == 4 && block_dim == 32) return swz<4, 32>(row, chunk);
+  if (chunks_per_row == 8 && block_dim == 16) return swz<8, 16>(row, chunk);
+  if (chunks_per_row == 4 && block_dim == 16) return swz<4, 16>(row, chunk);
+  return -1;
 }
 
 int64_t gemm_f16_schedule_dump(int64_t M, int64_t N, int64_t K, int64_t grid, int64_t* out,

@@ -31,6 +31,7 @@
 //     stream sums the slots of each tile in k order and writes C, so the
 //     result does not depend on timing and needs no flags or atomics.
 #include "gemm_kernels.h"
+#include "gemm_lds_layout.h"
 
 #include <hip/hip_runtime.h>
 
@@ -177,30 +178,6 @@ struct Cfg {
   static_assert(LDS_BYTES <= 163840, "gfx950 LDS limit");
   static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
 };
-
-// Position of logical 16-byte chunk `chunk` of tile row `row` inside the row.
-// A fragment read puts lane l on row l % DIM, chunk l / DIM of its k-step
-// (DIM = 32 or 16, the MFMA block height). On gfx950 the LDS serves a
-// ds_read_b128 in four passes of 16 lanes, and the passes are not runs of
-// consecutive lanes: measured, one pass holds lanes 0-3, 12-15, 20-23 and
-// 24-27, another 4-11, 16-19 and 28-31 (and the same two sets shifted by
-// 32). With 64 banks of 4 bytes a pass is conflict-free when its 16 lanes
-// land in 16 different 16-byte bank groups; each f below is one-to-one where
-// that requires it (checked exhaustively for every pass, k-step and block row).
-//   DIM 32, 128-byte rows: f = (row ^ (row >> 3)) & 7
-//   DIM 32,  64-byte rows: f = (row >> 2) & 3
-//   DIM 16, 128-byte rows: f = (row >> 1) & 7
-//   DIM 16,  64-byte rows: f = ((row >> 2) ^ ((row >> 1) & 2)) & 3
-template <int CHUNKS, int DIM>
-__device__ __forceinline__ int swz(int row, int chunk) {
-  if constexpr (DIM == 32) {
-    if constexpr (CHUNKS == 8) return chunk ^ ((row ^ (row >> 3)) & 7);
-    else return chunk ^ ((row >> 2) & 3);
-  } else {
-    if constexpr (CHUNKS == 8) return chunk ^ ((row >> 1) & 7);
-    else return chunk ^ (((row >> 2) ^ ((row >> 1) & 2)) & 3);
-  }
-}
 
 // s_waitcnt immediates (gfx9 layout): vmcnt bits [3:0] and [15:14],
 // expcnt [6:4], lgkmcnt [11:8]; a field at its maximum does not wait.

@@ -24,7 +24,8 @@ STATUS_NAMES = {
 EXPORTS = (
     "gemm_f16_f32_abt", "gemm_f16_f32_abt_workspace_size", "gemm_f16_f32_abt_ws",
     "gemm_status_string", "gemm_f16_f32_abt_describe", "gemm_f16_release_workspaces",
-    "gemm_f16_schedule_dump", "gemm_bf16_f32_abt", "gemm_bf16_f32_abt_workspace_size",
+    "gemm_f16_schedule_dump", "gemm_f16_lds_chunk", "gemm_bf16_f32_abt",
+    "gemm_bf16_f32_abt_workspace_size",
     "gemm_bf16_f32_abt_ws",
 )
 
@@ -68,6 +69,8 @@ def load(path: str = LIBRARY):
     lib.gemm_f16_release_workspaces.restype = None
     lib.gemm_f16_schedule_dump.argtypes = [i64, i64, i64, i64, p, i64, p, p]
     lib.gemm_f16_schedule_dump.restype = i64
+    lib.gemm_f16_lds_chunk.argtypes = [ctypes.c_int32] * 4
+    lib.gemm_f16_lds_chunk.restype = ctypes.c_int32
     if path == LIBRARY:
         _lib = lib
     return lib
@@ -123,6 +126,11 @@ def gemm_f16_f32_abt_describe(M, N, K) -> str:
 
 def gemm_f16_release_workspaces() -> None:
     load().gemm_f16_release_workspaces()
+
+
+def gemm_f16_lds_chunk(chunks_per_row, block_dim, row, chunk) -> int:
+    """LDS position of logical chunk `chunk` of tile row `row` (-1: bad arguments)."""
+    return load().gemm_f16_lds_chunk(chunks_per_row, block_dim, row, chunk)
 
 
 def gemm_f16_schedule_dump(M, N, K, grid=0):

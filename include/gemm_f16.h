@@ -133,6 +133,16 @@ void gemm_f16_release_workspaces(void);
 int64_t gemm_f16_schedule_dump(int64_t M, int64_t N, int64_t K, int64_t grid,
                                int64_t* out, int64_t cap, int64_t* k_iters, int64_t* tiles);
 
+/* Host-side view of the kernels' LDS layout (no device is touched): the
+ * position, within an LDS tile row of `chunks_per_row` 16-byte chunks (4 for
+ * 32-element k-stages, 8 for 64), at which the kernels store logical chunk
+ * `chunk` of tile row `row`, for MFMA block height `block_dim` (16 or 32).
+ * Returns -1 for other arguments. The same function runs in the kernels;
+ * tests use this to check that every row's chunks form a permutation and
+ * that the fragment reads (ds_read_b128) meet no LDS bank conflicts. */
+int32_t gemm_f16_lds_chunk(int32_t chunks_per_row, int32_t block_dim, int32_t row,
+                           int32_t chunk);
+
 
 #ifdef __cplusplus
 }

@@ -108,3 +108,23 @@ def test_device_uniform_on_the_cpu_generator():
     assert torch.isnan(full[:, 40:]).all() and not torch.isnan(p).any()
     with pytest.raises(ValueError):
         inputs.device_uniform(4, 8, 1, "cpu", ld=7)
+
+
+def test_generators_match_the_recorded_first_values():
+    """The first 16 bit patterns of every seeded generator, recorded in
+    tests/golden/inputs_first16.txt (written by make_inputs_golden.py)."""
+    import importlib.util
+    import os
+
+    here = os.path.join(os.path.dirname(__file__), "golden")
+    spec = importlib.util.spec_from_file_location(
+        "make_inputs_golden", os.path.join(here, "make_inputs_golden.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    recorded = {}
+    for line in open(os.path.join(here, "inputs_first16.txt")):
+        if line.strip() and not line.startswith("#"):
+            name, *vals = line.split()
+            recorded[name] = [int(v, 16) for v in vals]
+    now = {name: [int(x) for x in v] for name, v in mod.entries()}
+    assert now == recorded
