@@ -2,7 +2,7 @@
 """Benchmark of C = A * B^T (fp16 in, fp32 accumulate/out) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8192^3] [--dtype f16|bf16]
-                    [--no-cpu-baseline] [--no-long-k] [--shapes] [--vendor] [--calibrate-copy]
+                    [--no-cpu-baseline] [--no-extras] [--shapes] [--vendor] [--calibrate-copy]
 
 A step is one call of gemm_f16_f32_abt through the C ABI on synthetic
 operands already resident in HBM (uniform [-1, 1] fp16, seeds 1 and 2). The
@@ -15,7 +15,9 @@ peak (2.5 PFLOP/s dense).
 At 8192^3 the line also carries `long_k`: the two long-K workloads, 200
 back-to-back calls after 100 untimed ones, between one pair of HIP events
 (their main and reduce kernels and the gaps between calls), as fractions of
-peak beside the headline; `--no-long-k` leaves them out. The default 30
+peak beside the headline; and `pages_inputs`: 8192^3 again on the input kind
+the pages time on (integers in [-3, 3] from a hash), which draws less power
+on this board. `--no-extras` leaves both out. The default 30
 warm-up calls of the headline, and the 100 here, let the board's clocks
 settle: the first 20 or so calls of a new shape run several percent slower.
 
@@ -359,9 +361,10 @@ def main():
                     help="one of the five workloads, one of the pages' other shapes, "
                          "or any MxNxK")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-long-k", action="store_true",
-                    help="at 8192^3, skip the back-to-back timing of the two long-K workloads "
-                         "(profiling runs use this so their traces hold one shape)")
+    ap.add_argument("--no-extras", "--no-long-k", dest="no_extras", action="store_true",
+                    help="at 8192^3, skip the extra rows (the two long-K workloads and the "
+                         "hash-integer inputs); profiling runs use this so their traces hold "
+                         "one shape and one input kind")
     ap.add_argument("--no-telemetry", action="store_true",
                     help="skip the amd-smi clock/power sample after the timed region")
     ap.add_argument("--shapes", action="store_true",
@@ -463,7 +466,8 @@ def main():
             shapes.append(entry)
 
     long_k = []
-    if name == "8192^3" and not args.no_long_k:
+    pages_inputs = None
+    if name == "8192^3" and not args.no_extras:
         # The two long-K workloads, back to back like the headline, so every
         # bench line carries their fraction of peak as well (not the value).
         for n in ("2048x2048x16384", "1024x1024x65536"):
@@ -480,6 +484,22 @@ def main():
             log(f"[bench] {n}: {avg_us:.2f} us/call back to back "
                 f"({long_k[-1]['mfma_peak_frac'] * 100:.1f}% of peak)")
             del a, b, c
+            torch.cuda.empty_cache()
+        # The same workload on the input kind the pages time on (integers in
+        # [-3, 3] from a hash of the index): context for the data-dependent
+        # power draw, never the value.
+        if args.dtype == "f16":
+            a = torch.from_numpy(inputs.hash_int(M, K, 1)).to(dev)
+            b = torch.from_numpy(inputs.hash_int(N, K, 2)).to(dev)
+            avg_us = time_loop(torch, gemm, a, b, C, args.steps, args.warmup)
+            pages_inputs = {"workload": name, "inputs": "hash_int [-3, 3]",
+                            "us_per_call": round(avg_us, 3),
+                            "tflops": round(flops / (avg_us * 1e-6) / 1e12, 2),
+                            "mfma_peak_frac": round(flops / (avg_us * 1e-6) / 1e12 / PEAK_TFLOPS, 4),
+                            "calls": args.steps}
+            log(f"[bench] {name} on hash-integer inputs: {avg_us:.2f} us/call "
+                f"({pages_inputs['mfma_peak_frac'] * 100:.1f}% of peak)")
+            del a, b
             torch.cuda.empty_cache()
 
     vendor = None
@@ -510,7 +530,7 @@ def main():
                    "plan": gemm.gemm_f16_f32_abt_describe(M, N, K),
                    "source_hash": source_hash(), "library_md5": library_md5()},
         "roofline": roofline, "cpu_baseline": cpu, "shapes": shapes, "long_k": long_k,
-        "telemetry": tele,
+        "pages_inputs": pages_inputs, "telemetry": tele,
     }
     if vendor is not None:
         line["vendor_hipblaslt"] = vendor
