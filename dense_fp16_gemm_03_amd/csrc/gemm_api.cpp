@@ -142,10 +142,32 @@ bool tiled_eligible(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
 //     split so tiles x splits fills the CUs (each share keeps >= 64 k-steps);
 //   * smaller problems: 128x128 tiles, or 64x64 tiles when 128x128 ones
 //     would fill fewer than half the CUs, data-parallel (at these sizes the
-//     reduce pass of a split costs more than it gains).
+//     reduce pass of a split costs more than it gains);
+//   * several rounds of tiles whose last one is at most half full, with long
+//     K: whole rounds data-parallel, the tiles left by stream-K (DP_SK).
 Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                int64_t ldb, const float* C, int64_t ldc, int32_t cus, int32_t dt = DT_F16,
                bool allow_pack = true);
+
+// DP_SK: tiles below shared_base form whole data-parallel rounds of s.grid
+// tiles; the rest are shared by stream-K. Without a whole round it is plain
+// stream-K, and without a remainder plain data-parallel.
+void set_shared_base(Sched& s) {
+  if (s.mode != MODE_DP_SK) {
+    s.shared_base = 0;
+    return;
+  }
+  const int64_t whole = (int64_t)(s.tiles / s.grid) * s.grid;
+  if (whole == 0) {
+    s.mode = MODE_STREAM_K;
+    s.shared_base = 0;
+  } else if (whole == s.tiles) {
+    s.mode = MODE_DATA_PARALLEL;
+    s.shared_base = 0;
+  } else {
+    s.shared_base = (int32_t)whole;
+  }
+}
 
 // Operands the tiled kernels cannot load directly (a pointer off 16 bytes, a
 // row stride or K not a multiple of 8, a stride past the offset limit): for a
@@ -206,7 +228,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
     }
   }
   if (o.kid >= 0 && kernel_info(o.kid) && tiled_has(o.kid, dt)) kid = o.kid;
-  if (o.mode >= 0 && o.mode <= MODE_STREAM_K) mode = o.mode;
+  if (o.mode >= 0 && o.mode <= MODE_DP_SK) mode = o.mode;
   if (o.splits >= 1) splits = o.splits;
 
   if (!tiled_eligible(M, N, K, A, lda, B, ldb, kid)) {
@@ -225,6 +247,14 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
     return plan;
   }
   s.tiles = (int32_t)tiles;
+  // A last data-parallel round at most half full, with long K (>= 128
+  // k-iterations), is shared by all workgroups instead (whole rounds first,
+  // then stream-K over the tiles left); measured, the partial tiles and the
+  // reduce pass cost less than the idle CUs only from about that K.
+  if (o.mode < 0 && mode == MODE_DATA_PARALLEL && tiles > cus && s.k_iters >= 128) {
+    const int64_t left = tiles % cus;
+    if (left > 0 && 2 * left <= cus) mode = MODE_DP_SK;
+  }
   s.group_m = o.group > 0 ? o.group : 4;
   if (s.group_m > s.tiles_m) s.group_m = s.tiles_m;
   s.xcd_remap = o.xcd >= 0 ? (o.xcd != 0) : 1;
@@ -245,15 +275,20 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
   } else if (s.mode == MODE_SPLIT) {
     grid = std::min<int64_t>((int64_t)tiles * s.splits, resident);
     if (o.grid > 0) grid = std::min<int64_t>(grid, o.grid);
+  } else if (s.mode == MODE_DP_SK) {
+    grid = std::min<int64_t>((int64_t)tiles * s.k_iters, resident);
+    if (o.grid > 0) grid = std::min<int64_t>(grid, o.grid);
   } else {
     grid = std::min<int64_t>(tiles, resident);
     if (o.grid > 0) grid = std::min<int64_t>(o.grid, tiles);
   }
   s.grid = (int32_t)std::max<int64_t>(grid, 1);
+  set_shared_base(s);
   s.slots = max_shares(s);
   plan.kid = kid;
   if (s.mode != MODE_DATA_PARALLEL)
-    plan.workspace = (size_t)((int64_t)tiles * s.slots * ki->bm * ki->bn * 4);
+    plan.workspace =
+        (size_t)((int64_t)(tiles - s.shared_base) * s.slots * ki->bm * ki->bn * 4);
   return plan;
 }
 
@@ -262,6 +297,7 @@ const char* mode_name(int32_t m) {
     case MODE_DATA_PARALLEL: return "data_parallel";
     case MODE_SPLIT: return "split";
     case MODE_STREAM_K: return "stream_k";
+    case MODE_DP_SK: return "dp_stream_k";
     default: return "?";
   }
 }
@@ -530,8 +566,11 @@ int64_t gemm_f16_schedule_dump(int64_t M, int64_t N, int64_t K, int64_t grid, in
   if (plan.kid < 0 || plan.kid == KID_GENERAL) return -1;
   Sched s = plan.s;
   if (grid > 0) {
-    if (s.mode == MODE_STREAM_K && grid > (int64_t)s.tiles * s.k_iters) return -1;
+    if ((s.mode == MODE_STREAM_K || s.mode == MODE_DP_SK) &&
+        grid > (int64_t)s.tiles * s.k_iters)
+      return -1;
     s.grid = (int32_t)grid;
+    set_shared_base(s);  // DP_SK: its whole rounds depend on the grid
   }
   if (k_iters) *k_iters = s.k_iters;
   if (tiles) *tiles = s.tiles;

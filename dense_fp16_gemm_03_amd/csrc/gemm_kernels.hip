@@ -728,7 +728,8 @@ void gemm_tiled_kernel(GemmParams p) {
     } else {
       // One share of a tile: its partial goes to the workspace; the reduce
       // kernel that follows on the stream sums the shares into C.
-      write_partial<C>(p.partials + ((int64_t)seg.tile * p.s.slots + seg.index) * (C::BM * C::BN / 4),
+      write_partial<C>(p.partials + ((int64_t)(seg.tile - p.s.shared_base) * p.s.slots + seg.index) *
+                                        (C::BM * C::BN / 4),
                        acc, wave, lane);
     }
   }
@@ -898,7 +899,8 @@ void gemm_pingpong_kernel(GemmParams p) {
     } else {
       // write_partial issues epilogue_stores<C>() buffer stores as well.
       stores_behind = more;
-      write_partial<C>(p.partials + ((int64_t)done.tile * p.s.slots + done.index) * (C::BM * C::BN / 4),
+      write_partial<C>(p.partials + ((int64_t)(done.tile - p.s.shared_base) * p.s.slots + done.index) *
+                                        (C::BM * C::BN / 4),
                        acc, wave, lane);
     }
     // Matches group 1's extra barrier at the start of the unit.
@@ -910,18 +912,18 @@ void gemm_pingpong_kernel(GemmParams p) {
 // Shares of output tile t under schedule s (1: the tile was stored directly).
 __device__ __forceinline__ int tile_shares(const Sched& s, int t) {
   if (s.mode == MODE_SPLIT) return s.splits;
-  if (s.mode != MODE_STREAM_K) return 1;
-  const int64_t lo = (int64_t)t * s.k_iters;
+  if ((s.mode != MODE_STREAM_K && s.mode != MODE_DP_SK) || t < s.shared_base) return 1;
+  const int64_t lo = (int64_t)(t - s.shared_base) * s.k_iters;
   return (int)(sk_owner(s, lo + s.k_iters - 1) - sk_owner(s, lo) + 1);
 }
 
 // Reduce pass for split-K / stream-K: workgroup b handles slice b % slices
-// of tile b / slices. Partials are summed in k order, so the result does not
+// of tile shared_base + b / slices. Partials are summed in k order, so the result does not
 // depend on timing.
 template <class C>
 __global__ __launch_bounds__(kReduceThreads) void gemm_reduce_kernel(GemmParams p, int32_t slices) {
   constexpr int L = C::BM * C::BN / 4;
-  const int t = blockIdx.x / slices;
+  const int t = p.s.shared_base + (int)(blockIdx.x / slices);
   const int slice = blockIdx.x % slices;
   const int shares = tile_shares(p.s, t);
   if (shares <= 1) return;
@@ -929,8 +931,8 @@ __global__ __launch_bounds__(kReduceThreads) void gemm_reduce_kernel(GemmParams 
   tile_coords(p.s, t, &tm, &tn);
   const int begin = (int)((int64_t)slice * L / slices);
   const int end = (int)((int64_t)(slice + 1) * L / slices);
-  reduce_range<C>(p, p.partials + (int64_t)t * p.s.slots * L, shares, begin, end, tm * C::BM,
-                  tn * C::BN);
+  reduce_range<C>(p, p.partials + (int64_t)(t - p.s.shared_base) * p.s.slots * L, shares, begin,
+                  end, tm * C::BM, tn * C::BN);
 }
 
 // General kernel: any shape, stride and (element-natural) alignment. 4 waves
@@ -1071,10 +1073,12 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t stream) {
   if (e != hipSuccess || p.s.mode == MODE_DATA_PARALLEL) return e;
   // Slices per tile: enough workgroups to cover the CUs, at least 4 KiB each.
   const int max_slices = C::BM * C::BN / 4 / 256;
-  int slices = (256 + p.s.tiles - 1) / p.s.tiles;
+  const int shared_tiles = p.s.tiles - p.s.shared_base;  // tiles that may have partials
+  if (shared_tiles <= 0) return e;
+  int slices = (256 + shared_tiles - 1) / shared_tiles;
   if (slices > max_slices) slices = max_slices;
   if (slices < 1) slices = 1;
-  hipLaunchKernelGGL(gemm_reduce_kernel<C>, dim3(p.s.tiles * slices), dim3(kReduceThreads), 0,
+  hipLaunchKernelGGL(gemm_reduce_kernel<C>, dim3(shared_tiles * slices), dim3(kReduceThreads), 0,
                      stream, p, slices);
   return hipGetLastError();
 }

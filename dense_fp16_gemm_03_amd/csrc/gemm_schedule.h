@@ -3,7 +3,7 @@
 // integer arithmetic, callable from both sides, so the model the tests check
 // is the very code the kernels run.
 //
-// Three modes, after the per-shape program rule of "SASS-Level Kernel
+// Four modes, after the per-shape program rule of "SASS-Level Kernel
 // Generation for Blackwell" (section "Inside the kernels"), which picks for
 // each shape between a persistent grid over whole tiles, a split of K and
 // stream-K:
@@ -14,6 +14,10 @@
 //   STREAM_K       the k-iterations of all tiles, laid end to end, are cut
 //                  into one contiguous range per workgroup; a range may end
 //                  part-way through a tile and start the next one.
+//   DP_SK          whole rounds of tiles (grid tiles each) data-parallel,
+//                  then STREAM_K over the tiles left, so a last round that
+//                  would keep few workgroups busy is shared by all of them.
+//                  Only those last tiles can have partial tiles.
 // The shares of a tile are not added in place (the page adds them in L2):
 // each share writes its fp32 partial tile to a workspace slot, and a reduce
 // kernel launched after the main kernel on the same stream sums every tile's
@@ -31,7 +35,12 @@
 
 namespace g16 {
 
-enum SchedMode : int32_t { MODE_DATA_PARALLEL = 0, MODE_SPLIT = 1, MODE_STREAM_K = 2 };
+enum SchedMode : int32_t {
+  MODE_DATA_PARALLEL = 0,
+  MODE_SPLIT = 1,
+  MODE_STREAM_K = 2,
+  MODE_DP_SK = 3  // whole data-parallel rounds, then stream-K over the tiles left
+};
 enum SegRole : int32_t { ROLE_ONLY = 0, ROLE_SHARED = 1 };
 
 struct Sched {
@@ -43,6 +52,9 @@ struct Sched {
   int32_t group_m;                  // tile order: bands of group_m tile rows
   int32_t xcd_remap;                // 1: renumber workgroups XCD by XCD (virtual_wg)
   int32_t slots;                    // partial-tile slots per tile in the workspace
+  int32_t shared_base;              // first tile that may be shared (DP_SK: the tiles of
+                                    // the whole data-parallel rounds come before it);
+                                    // partial tiles are indexed from it
 };
 
 struct Segment {
@@ -80,16 +92,24 @@ G16_HD void tile_coords(const Sched& s, int32_t idx, int32_t* tm, int32_t* tn) {
   *tn = r / rows;
 }
 
-// STREAM_K: first k-iteration (over all tiles) of virtual workgroup v.
-G16_HD int64_t sk_start(const Sched& s, int64_t v) {
-  const int64_t total = (int64_t)s.tiles * s.k_iters;
-  return v * total / s.grid;
+// STREAM_K and DP_SK: k-iterations of the stream-K region (tiles from
+// shared_base on, laid end to end; iteration 0 is the first of tile
+// shared_base).
+G16_HD int64_t sk_total(const Sched& s) {
+  return (int64_t)(s.tiles - s.shared_base) * s.k_iters;
 }
 
-// STREAM_K: the workgroup whose (non-empty) range holds iteration i.
+// Workgroups that take part in the stream-K region: all of the grid, or as
+// many as it has iterations (DP_SK's region can be smaller than the grid), so
+// every range is non-empty and the owners of a tile are consecutive.
+G16_HD int64_t sk_grid(const Sched& s) { return min_of<int64_t>(s.grid, sk_total(s)); }
+
+// First stream-K iteration of virtual workgroup v (v <= sk_grid).
+G16_HD int64_t sk_start(const Sched& s, int64_t v) { return v * sk_total(s) / sk_grid(s); }
+
+// The workgroup whose range holds stream-K iteration i.
 G16_HD int64_t sk_owner(const Sched& s, int64_t i) {
-  const int64_t total = (int64_t)s.tiles * s.k_iters;
-  return ((i + 1) * s.grid - 1) / total;
+  return ((i + 1) * sk_grid(s) - 1) / sk_total(s);
 }
 
 // Number of units (DATA_PARALLEL, SPLIT) or segments a workgroup walks is
@@ -97,17 +117,33 @@ G16_HD int64_t sk_owner(const Sched& s, int64_t i) {
 //
 // DATA_PARALLEL / SPLIT: the n-th unit of virtual workgroup v is v + n*grid.
 // STREAM_K: the n-th segment of v, counted from the end of v's range.
+// DP_SK: first the whole tiles v + n*grid below shared_base (a multiple of
+// grid), then v's stream-K segments over the remaining tiles.
 G16_HD bool seg_at(const Sched& s, int32_t v, int32_t n, Segment* out) {
-  if (s.mode == MODE_STREAM_K) {
+  if (s.mode == MODE_STREAM_K || s.mode == MODE_DP_SK) {
+    const int32_t rounds = s.mode == MODE_DP_SK ? s.shared_base / s.grid : 0;
+    if (n < rounds) {
+      const int32_t t = v + n * s.grid;
+      out->tile = t;
+      tile_coords(s, t, &out->tm, &out->tn);
+      out->k_begin = 0;
+      out->k_end = s.k_iters;
+      out->contributors = 1;
+      out->index = 0;
+      out->role = ROLE_ONLY;
+      return true;
+    }
+    n -= rounds;
+    if (v >= sk_grid(s)) return false;  // no stream-K range for this workgroup
     const int64_t a = sk_start(s, v);
     int64_t b = sk_start(s, (int64_t)v + 1);
     for (int32_t i = 0; b > a; ++i) {
-      const int64_t t = (b - 1) / s.k_iters;
+      const int64_t t = (b - 1) / s.k_iters;  // tile within the stream-K region
       const int64_t tile_lo = t * s.k_iters;
       const int64_t lo = max_of(a, tile_lo);
       if (i == n) {
-        out->tile = (int32_t)t;
-        tile_coords(s, (int32_t)t, &out->tm, &out->tn);
+        out->tile = (int32_t)(s.shared_base + t);
+        tile_coords(s, out->tile, &out->tm, &out->tn);
         out->k_begin = (int32_t)(lo - tile_lo);
         out->k_end = (int32_t)(b - tile_lo);
         const int64_t first = sk_owner(s, tile_lo);
@@ -143,9 +179,9 @@ namespace g16 {
 // Most shares any tile has under schedule s (the workspace slots per tile).
 inline int32_t max_shares(const Sched& s) {
   if (s.mode == MODE_SPLIT) return s.splits;
-  if (s.mode != MODE_STREAM_K) return 1;
+  if (s.mode != MODE_STREAM_K && s.mode != MODE_DP_SK) return 1;
   int64_t most = 1;
-  for (int64_t t = 0; t < s.tiles; ++t) {
+  for (int64_t t = 0; t < (int64_t)s.tiles - s.shared_base; ++t) {
     const int64_t lo = t * s.k_iters;
     const int64_t c = sk_owner(s, lo + s.k_iters - 1) - sk_owner(s, lo) + 1;
     if (c > most) most = c;

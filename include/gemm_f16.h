@@ -52,7 +52,8 @@ typedef enum {
  * an operand breaks these rules and M*N*K >= 2^22, a pack kernel first copies
  * it into the workspace as rows of K rounded up to 8 elements (zero past K)
  * and the tiled kernels run on the copy; smaller products take a slower
- * general kernel. Split-K / stream-K plans write fp32 partial tiles
+ * general kernel. Split-K and stream-K plans (the latter also for the tiles
+ * left after whole data-parallel rounds) write fp32 partial tiles
  * to a workspace and a second kernel on the same stream sums them, in a fixed
  * (k) order, into C, so results do not depend on timing. The workspace is
  * library-owned, allocated once per (device, stream) on first use and grown
@@ -120,7 +121,7 @@ void gemm_f16_release_workspaces(void);
 /* Host-side schedule model (no device is touched): fills out[] with one row
  * of 7 int64 per (workgroup, segment) of the persistent schedule for
  * (M, N, K) with `grid` workgroups (grid <= 0: the plan's own grid; only
- * stream-K and data-parallel plans accept another grid):
+ * data-parallel, stream-K and rounds-then-stream-K plans accept another grid):
  *   { workgroup, tile, k_iter_begin, k_iter_end, role, shares, index }
  * role 0 = the tile's only unit (stores C directly); role 1 = one of `shares`
  * units of a tile, `index` its position in k order (writes its partial tile

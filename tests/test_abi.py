@@ -192,6 +192,12 @@ SCHED_CASES = [
     (5000, 300, 2048, "mode=1,splits=3"),
     (5000, 300, 2048, "mode=1,splits=3,grid=50"),   # split-K over several rounds
     (3000, 2900, 1024, None),
+    (4608, 4608, 2048, "mode=3"),           # one data-parallel round, stream-K tail
+    (4608, 4608, 2048, "mode=3,grid=100"),  # three whole rounds of 100, 24 tiles shared
+    (5000, 300, 2048, "mode=3,grid=7"),     # ranges of the tail cross tile ends
+    (3072, 3072, 4096, "mode=3"),           # no whole round: plain stream-K
+    (4096, 4096, 4096, "mode=3"),           # no remainder: plain data-parallel
+    (630, 621, 80, "mode=3,kid=6,grid=92"),  # 16 stream-K iterations for 92 workgroups
 ]
 
 
@@ -203,9 +209,23 @@ def test_schedule_covers_once(lib, monkeypatch, M, N, K, plan):
     assert check_schedule(rows.tolist(), k_iters, tiles) == []
     if plan and "mode=2" in plan:
         assert "stream_k" in gemm.gemm_f16_f32_abt_describe(M, N, K)
+    if plan and "mode=3" in plan:
+        text = gemm.gemm_f16_f32_abt_describe(M, N, K)
+        grid = int(plan.split("grid=")[1]) if "grid" in plan else 256
+        whole_rounds = tiles // grid
+        if tiles % grid == 0:
+            assert "mode=data_parallel" in text
+        elif whole_rounds == 0:
+            assert "mode=stream_k" in text
+        else:
+            assert "mode=dp_stream_k" in text and f"grid={grid}" in text
+            # whole tiles of the data-parallel rounds are never shared
+            base = whole_rounds * grid
+            assert all(r[1] >= base or r[5] == 1 for r in rows.tolist())
+            assert any(r[1] >= base and r[5] > 1 for r in rows.tolist())
 
 
-@pytest.mark.parametrize("M,N,K,plan", SCHED_CASES[:3] + SCHED_CASES[6:7])
+@pytest.mark.parametrize("M,N,K,plan", SCHED_CASES[:3] + SCHED_CASES[6:7] + SCHED_CASES[12:15])
 def test_schedule_model_detects_dropped_unit(lib, monkeypatch, M, N, K, plan):
     """Dropping any one segment, or duplicating one, must fail the model."""
     if plan:
@@ -235,6 +255,23 @@ def test_default_plans(lib):
         assert rows[:, 0].max() < 256
 
 
+@pytest.mark.parametrize("M,N,K,mode", [
+    (4608, 4608, 8192, "dp_stream_k"),   # 324 tiles: 68 left after one round, long K
+    (4352, 4352, 4096, "dp_stream_k"),   # 289 tiles: 33 left
+    (4608, 4608, 2048, "data_parallel"),  # 64 k-iterations: the reduce costs more
+    (5120, 5120, 4096, "data_parallel"),  # 400 tiles: last round more than half full
+    (8192, 8192, 8192, "data_parallel"),  # whole rounds only
+    (2048, 2048, 16384, "split"),         # fewer tiles than CUs
+])
+def test_default_tail_rule(lib, M, N, K, mode):
+    """Several rounds of tiles with a last round at most half full and long K
+    run whole rounds data-parallel and share the tiles left (stream-K); the
+    default plan still covers every (tile, k-iteration) once."""
+    assert f"mode={mode} " in gemm.gemm_f16_f32_abt_describe(M, N, K) + " "
+    rows, k_iters, tiles = gemm.gemm_f16_schedule_dump(M, N, K)
+    assert check_schedule(rows.tolist(), k_iters, tiles) == []
+
+
 def test_plan_override_parsed_on_many_threads(lib, monkeypatch):
     """The override is parsed on every plan; ctypes releases the GIL, so
     these calls run concurrently and every one must see the same plan."""
@@ -258,3 +295,19 @@ def test_plan_override_parsed_on_many_threads(lib, monkeypatch):
     for t in threads:
         t.join()
     assert not bad, bad[:2]
+
+
+def test_schedule_model_random_stream_k_plans(lib, monkeypatch):
+    """Seeded random shapes, kernels and grids under stream-K and under whole
+    data-parallel rounds then stream-K: the host model of every plan covers
+    each (tile, k-iteration) once and numbers each tile's shares 0..s-1 in k
+    order (a grid larger than the stream-K iterations once broke that)."""
+    rng = np.random.default_rng(7)
+    for _ in range(300):
+        M, N = int(rng.integers(1, 3000)), int(rng.integers(1, 3000))
+        K = int(rng.integers(1, 375)) * 8
+        kid = int(rng.choice([0, 4, 6, 16, 18, 25, 26, 27, 29, 33]))
+        plan = f"kid={kid},mode={int(rng.choice([2, 3]))},grid={int(rng.integers(1, 300))}"
+        monkeypatch.setenv("GEMM_F16_PLAN", plan)
+        rows, k_iters, tiles = gemm.gemm_f16_schedule_dump(M, N, K)
+        assert check_schedule(rows.tolist(), k_iters, tiles) == [], (M, N, K, plan)

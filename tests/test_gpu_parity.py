@@ -170,6 +170,26 @@ def test_page_shape_parity(name):
         assert_exact(got[rows, cols], ref, f"{name} integer")
 
 
+@pytest.mark.parametrize("M,N,K", [(4608, 4608, 8192), (4352, 4352, 4096)])
+def test_default_rounds_then_stream_k(M, N, K):
+    """Shapes whose last round of 256x256 tiles is at most half full, with long
+    K, run whole data-parallel rounds and then stream-K over the tiles left:
+    integer inputs bit-exact on sampled points (rows and columns through
+    the shared tiles), and k-block weights, where a missing or doubled
+    share changes every element."""
+    text = gemm.gemm_f16_f32_abt_describe(M, N, K)
+    log(f"  plan: {text}")
+    assert "mode=dp_stream_k" in text
+    A, B = operands((M, N, K), "integer")
+    got = run(A, B)
+    rows, cols = sample_points(M, N, n_rand=2000)
+    ref, _ = oracle.gemm_abt_elems(A, B, rows, cols)
+    assert_exact(got[rows, cols], ref, f"{M}x{N}x{K} integer")
+    w = 1 + (np.arange(K) // 64) % 7
+    got = run(inputs.ones(M, K), inputs.kblock_weights(N, K, 64))
+    assert np.all(got == float(w.sum())), f"k-block sum: got {np.unique(got)[:5]}"
+
+
 def test_hash_int_inputs():
     """Integers in [-3, 3] from a hash of the index: exact."""
     M, N, K = 1024, 1024, 4096
@@ -337,6 +357,10 @@ PLANS = [f"kid={k}" for k in range(35)] + [
     # stores left in flight) with ragged ones (element stores).
     "kid=25,grid=2", "kid=26,grid=3", "kid=27,grid=3", "kid=27,grid=1",
     "kid=27,mode=1,splits=2,grid=7", "kid=28,grid=4", "kid=29,grid=5",
+    # Whole data-parallel rounds, then stream-K over the tiles left (the
+    # forced grids make whole rounds at this size).
+    "kid=27,mode=3,grid=4", "kid=26,mode=3,grid=5", "kid=16,mode=3,grid=7",
+    "kid=18,mode=3,grid=50", "kid=4,mode=3,grid=11", "kid=29,mode=3,grid=8",
 ]
 
 

@@ -2,8 +2,8 @@
 
 Each case draws, from one fixed seed, a shape (M, N up to 700, K up to 2200),
 row strides and pointer offsets for A, B and C, the operand type (binary16 or
-bfloat16) and a forced plan (kernel id, data-parallel / split-K / stream-K,
-grid). Inputs are integers in {-2..2}, where every partial sum is exact in
+bfloat16) and a forced plan (kernel id, data-parallel / split-K / stream-K /
+data-parallel rounds then stream-K, grid). Inputs are integers in {-2..2}, where every partial sum is exact in
 fp32, so C must equal the CPU reference bit for bit whatever the summation
 order. C sits inside a NaN-filled buffer with padding columns on both sides:
 after the call the padding must still be NaN (no store outside C).
@@ -50,11 +50,11 @@ def draw(i):
     dtype = "bf16" if rng.random() < 0.4 else "f16"
     kid = int(rng.choice(KIDS_BF16)) if dtype == "bf16" else int(rng.integers(0, KIDS_F16))
     plan = f"kid={kid}"
-    mode = int(rng.integers(0, 3))
+    mode = int(rng.integers(0, 4))
     if mode == 1:
         plan += f",mode=1,splits={int(rng.integers(2, 9))}"
-    elif mode == 2:
-        plan += ",mode=2"
+    elif mode in (2, 3):  # stream-K, or whole data-parallel rounds then stream-K
+        plan += f",mode={mode}"
     if rng.random() < 0.5:
         plan += f",grid={int(rng.integers(1, 300))}"
     if rng.random() < 0.1:
