@@ -143,8 +143,9 @@ bool tiled_eligible(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
 //   * smaller problems: 128x128 tiles, or 64x64 tiles when 128x128 ones
 //     would fill fewer than half the CUs, data-parallel (at these sizes the
 //     reduce pass of a split costs more than it gains);
-//   * several rounds of tiles whose last one is at most half full, with long
-//     K: whole rounds data-parallel, the tiles left by stream-K (DP_SK).
+//   * more 256x256 tiles than CUs, when the last round's idle CUs times the
+//     k-iterations is large enough: whole rounds data-parallel, the tiles
+//     left by stream-K (DP_SK).
 Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                int64_t ldb, const float* C, int64_t ldc, int32_t cus, int32_t dt = DT_F16,
                bool allow_pack = true);
@@ -247,13 +248,14 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
     return plan;
   }
   s.tiles = (int32_t)tiles;
-  // A last data-parallel round at most half full, with long K (>= 128
-  // k-iterations), is shared by all workgroups instead (whole rounds first,
-  // then stream-K over the tiles left); measured, the partial tiles and the
-  // reduce pass cost less than the idle CUs only from about that K.
-  if (o.mode < 0 && mode == MODE_DATA_PARALLEL && tiles > cus && s.k_iters >= 128) {
+  // After whole data-parallel rounds of 256x256 tiles, the tiles left are
+  // shared by all workgroups (stream-K) when the CUs a last data-parallel
+  // round would leave idle cost more than sharing does. Measured: the partial
+  // tiles and the reduce pass cost about 40 us, an idle CU about 0.85 us per
+  // k-iteration, so sharing pays from (idle CUs / CUs) * k_iters of about 44.
+  if (o.mode < 0 && mode == MODE_DATA_PARALLEL && kid == KID_LARGE && tiles > cus) {
     const int64_t left = tiles % cus;
-    if (left > 0 && 2 * left <= cus) mode = MODE_DP_SK;
+    if (left > 0 && (cus - left) * (int64_t)s.k_iters >= 44 * (int64_t)cus) mode = MODE_DP_SK;
   }
   s.group_m = o.group > 0 ? o.group : 4;
   if (s.group_m > s.tiles_m) s.group_m = s.tiles_m;

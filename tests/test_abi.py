@@ -256,17 +256,20 @@ def test_default_plans(lib):
 
 
 @pytest.mark.parametrize("M,N,K,mode", [
-    (4608, 4608, 8192, "dp_stream_k"),   # 324 tiles: 68 left after one round, long K
+    (4608, 4608, 8192, "dp_stream_k"),   # 324 tiles: 68 left; 188 idle CUs x 256 k-iters
     (4352, 4352, 4096, "dp_stream_k"),   # 289 tiles: 33 left
-    (4608, 4608, 2048, "data_parallel"),  # 64 k-iterations: the reduce costs more
-    (5120, 5120, 4096, "data_parallel"),  # 400 tiles: last round more than half full
+    (4608, 4608, 2048, "dp_stream_k"),   # 188 idle x 64 k-iters: 47 per CU
+    (5120, 5120, 4096, "dp_stream_k"),   # 400 tiles: 112 idle x 128
+    (6400, 6400, 2048, "data_parallel"),  # 625 tiles: 143 idle x 64 = 36 per CU
     (8192, 8192, 8192, "data_parallel"),  # whole rounds only
+    (4096, 4096, 4096, "data_parallel"),  # exactly one round
     (2048, 2048, 16384, "split"),         # fewer tiles than CUs
 ])
 def test_default_tail_rule(lib, M, N, K, mode):
-    """Several rounds of tiles with a last round at most half full and long K
-    run whole rounds data-parallel and share the tiles left (stream-K); the
-    default plan still covers every (tile, k-iteration) once."""
+    """With more tiles than CUs, the tiles left after whole data-parallel
+    rounds are shared by stream-K when the last round's idle CUs times the
+    k-iterations is at least 44 per CU; the default plan still covers every
+    (tile, k-iteration) once."""
     assert f"mode={mode} " in gemm.gemm_f16_f32_abt_describe(M, N, K) + " "
     rows, k_iters, tiles = gemm.gemm_f16_schedule_dump(M, N, K)
     assert check_schedule(rows.tolist(), k_iters, tiles) == []

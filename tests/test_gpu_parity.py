@@ -422,15 +422,20 @@ def test_transpose_invariant():
     assert_tol(run(B, A).T, ref, S, "uniform transpose")
 
 
-@pytest.mark.parametrize("name", ["2048x2048x16384", "1024x1024x65536"])
+@pytest.mark.parametrize("name", ["2048x2048x16384", "1024x1024x65536", "4352x4352x4096"])
 def test_repeat_and_caller_workspace(name):
     """Split-K / stream-K results are bitwise repeatable (partials are summed in
     k order), also on uniform inputs, and a caller workspace holding garbage
-    gives the same C."""
-    M, N, K = WORKLOADS[name]
+    gives the same C. 4352^2 x 4096 runs whole data-parallel rounds and then
+    stream-K over the 33 tiles left, whose partials alone use the workspace."""
+    M, N, K = WORKLOADS[name] if name in WORKLOADS else tuple(map(int, name.split("x")))
+    log(f"  plan: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
     A, B = operands((M, N, K), "uniform")
     At, Bt = to_dev(A), to_dev(B)
     first = run(At, Bt)
+    rows, cols = sample_points(M, N, n_rand=2000)
+    ref, S = oracle.gemm_abt_elems(A, B, rows, cols)
+    assert_tol(first[rows, cols], ref, S, f"{name} uniform")
     second = run(At, Bt, fill=-7.0)
     assert np.array_equal(first, second)
     nbytes = gemm.gemm_f16_f32_abt_workspace_size(M, N, K)
