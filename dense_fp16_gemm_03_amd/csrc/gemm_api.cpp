@@ -461,11 +461,14 @@ gemm_status_t gemm_bf16_f32_abt(int64_t M, int64_t N, int64_t K, const void* A, 
 
 size_t gemm_f16_f32_abt_workspace_size(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K < 0) return 0;
-  // Aligned operands with K as the row stride: the plan the fast path takes.
+  // Aligned operands with K as the row stride: the plan the fast path takes,
+  // for the current device's CU count (a partitioned device has fewer CUs and
+  // may plan differently).
+  int dev = 0;
+  const int32_t cus = hipGetDevice(&dev) == hipSuccess ? device_cus(dev) : kDefaultCUs;
   const void* aligned = (const void*)(uintptr_t)256;
   const int64_t ld = K % 8 ? K + (8 - K % 8) : K;
-  const Plan plan = make_plan(M, N, K, aligned, ld, aligned, ld, (const float*)aligned, N,
-                              kDefaultCUs);
+  const Plan plan = make_plan(M, N, K, aligned, ld, aligned, ld, (const float*)aligned, N, cus);
   // With K not a multiple of 8 the rows of both operands are packed (no row
   // stride makes them 16-byte aligned), and this includes the copies. Other
   // misaligned operands pack only into a caller workspace large enough for

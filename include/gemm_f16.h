@@ -65,9 +65,11 @@ gemm_status_t gemm_f16_f32_abt(int64_t M, int64_t N, int64_t K,
                                const void* B, int64_t ldb,
                                float* C, int64_t ldc, void* stream);
 
-/* Bytes of workspace gemm_f16_f32_abt_ws needs for this shape (0 if none),
- * for 16-byte aligned operands with row strides a multiple of 8; when K is
- * not a multiple of 8 it includes the packed copies of both operands. */
+/* Bytes of workspace gemm_f16_f32_abt_ws needs for this shape (0 if none) on
+ * the current device (its CU count sets the plan; 256 when no device is
+ * visible), for 16-byte aligned operands with row strides a multiple of 8;
+ * when K is not a multiple of 8 it includes the packed copies of both
+ * operands. */
 size_t gemm_f16_f32_abt_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /* As gemm_f16_f32_abt, with a caller-owned device workspace of at least
@@ -109,8 +111,9 @@ gemm_status_t gemm_bf16_f32_abt_ws(int64_t M, int64_t N, int64_t K,
 /* Static text for a status code (never NULL). */
 const char* gemm_status_string(gemm_status_t s);
 
-/* Writes a one-line description of the plan chosen for (M, N, K) into the
- * host buffer buf (NUL-terminated, truncated to len). Touches no device.
+/* Writes a one-line description of the plan chosen for (M, N, K) on a
+ * 256-CU device (a whole MI355X) into the host buffer buf (NUL-terminated,
+ * truncated to len). Touches no device.
  * Same size limits as gemm_f16_f32_abt (GEMM_ERR_NOT_SUPPORTED beyond them). */
 gemm_status_t gemm_f16_f32_abt_describe(int64_t M, int64_t N, int64_t K, char* buf, size_t len);
 
@@ -120,7 +123,7 @@ void gemm_f16_release_workspaces(void);
 
 /* Host-side schedule model (no device is touched): fills out[] with one row
  * of 7 int64 per (workgroup, segment) of the persistent schedule for
- * (M, N, K) with `grid` workgroups (grid <= 0: the plan's own grid; only
+ * (M, N, K) on a 256-CU device with `grid` workgroups (grid <= 0: the plan's own grid; only
  * data-parallel, stream-K and rounds-then-stream-K plans accept another grid):
  *   { workgroup, tile, k_iter_begin, k_iter_end, role, shares, index }
  * role 0 = the tile's only unit (stores C directly); role 1 = one of `shares`
