@@ -16,7 +16,8 @@ namespace g16 {
 // X(id, enum name, BM, BN, BK, STAGES, WGM, WGN, MFMA, RS, PP); RS 1 issues
 // each next-k-step fragment read right after the last use of the one it
 // replaces; PP 1 selects the ping-pong main loop (two wave groups, one
-// computing while the other reads LDS and issues loads).
+// computing while the other reads LDS and issues loads), PP 2 its form with
+// two stages 64 wide in k (whole 128-byte rows per load).
 #define G16_TILED_KERNELS(X)                                       \
   X(0, KID_256x256x64_S2_W4, 256, 256, 64, 2, 2, 2, 32, 0, 0)            \
   X(1, KID_256x256x32_S4_W4, 256, 256, 32, 4, 2, 2, 32, 0, 0)            \
@@ -52,11 +53,12 @@ namespace g16 {
   X(31, KID_64x64x32_S10_W4_M16, 64, 64, 32, 10, 2, 2, 16, 0, 0)       \
   X(32, KID_128x64x64_S6_W4_M16, 128, 64, 64, 6, 2, 2, 16, 0, 0)       \
   X(33, KID_64x64x64_S8_W4, 64, 64, 64, 8, 2, 2, 32, 0, 0)             \
-  X(34, KID_128x128x64_S4_W4_M16_RS, 128, 128, 64, 4, 2, 2, 16, 1, 0)
+  X(34, KID_128x128x64_S4_W4_M16_RS, 128, 128, 64, 4, 2, 2, 16, 1, 0) \
+  X(35, KID_256x256x64_S2_W8_M16_PP, 256, 256, 64, 2, 2, 4, 16, 0, 2)
 
 // Kernel ids also built for bfloat16 operands (the shape rule's picks, and
 // the other ping-pong depths).
-#define G16_BF16_KERNELS(X) X(16) X(18) X(25) X(26) X(27)
+#define G16_BF16_KERNELS(X) X(16) X(18) X(25) X(26) X(27) X(35)
 
 // Operand element types.
 enum DType : int32_t { DT_F16 = 0, DT_BF16 = 1 };
@@ -64,7 +66,7 @@ enum DType : int32_t { DT_F16 = 0, DT_BF16 = 1 };
 #define G16_KID_ENUM(id, name, ...) name = id,
 enum KernelId : int32_t {
   G16_TILED_KERNELS(G16_KID_ENUM)
-  KID_COUNT = 35,
+  KID_COUNT = 36,
   KID_GENERAL = 100  // any shape and alignment, 64 x 64 tiles, no LDS
 };
 #undef G16_KID_ENUM

@@ -140,7 +140,8 @@ struct Mma<16, DT_BF16> : MmaShape<16> {
 // evenly over the k-step's MFMAs; 1: each right after the last MFMA that uses
 // the fragment it replaces, so the current and next fragments barely overlap
 // in registers (for register-bound variants).
-// PP_: 1 selects the ping-pong main loop (gemm_pingpong_kernel, 8 waves).
+// PP_: 1 selects the ping-pong main loop (gemm_pingpong_kernel, 8 waves), 2 the
+// same loop over two 64-wide stages (gemm_pingpong64_kernel).
 // DT_: operand element type (DT_F16 or DT_BF16).
 template <int BM_, int BN_, int BK_, int STAGES_, int WGM_, int WGN_, int MI_ = 32, int RS_ = 0,
           int PP_ = 0, int DT_ = DT_F16>
@@ -909,6 +910,121 @@ void gemm_pingpong_kernel(GemmParams p) {
   }
 }
 
+// Ping-pong main loop over stages 64 wide in k, two of them in LDS (128 KiB),
+// with the same two wave groups and phases as gemm_pingpong_kernel, one
+// memory and one compute phase per 32-wide k-step. A stage's rows are 128
+// bytes, a whole cache line each: every load of a wave covers 8 rows x 128
+// bytes instead of 16 rows x 64 bytes, which the memory system delivers at
+// nearly twice the rate (same addresses otherwise).
+//   k-step 0 of stage it: read its fragments, issue this wave's loads of
+//     stage it + 1 into the other buffer (last read in the memory phase just
+//     before the previous barrier, so free);
+//   k-step 1 of stage it: read its fragments, wait until stage it + 1 has
+//     landed.
+// A load is thus awaited one k-step after it was issued, as in the 32-wide
+// three-stage ring. Between units the next unit's first stage goes out
+// before the finished unit's stores, which stay in flight through the next
+// unit's first wait; the wait for its stage 1 drains them.
+template <class C>
+__global__ __launch_bounds__(C::THREADS)
+__attribute__((amdgpu_waves_per_eu(C::WAVES_PER_EU, C::WAVES_PER_EU)))
+void gemm_pingpong64_kernel(GemmParams p) {
+  static_assert(C::WAVES == 8, "ping-pong pairs two waves per SIMD");
+  static_assert(C::STAGES == 2 && C::KSTEPS == 2, "two stages of two k-steps");
+  constexpr int kStores = epilogue_stores<C>();
+  static_assert(C::LOADS + kStores <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool late = wave >= 4;  // group 1
+  const int wm = wave / C::WGN;
+  const int wn = wave % C::WGN;
+  const int v = virtual_wg(blockIdx.x, p.s.grid, p.s.xcd_remap);
+
+  Segment seg;
+  if (!seg_at_uniform(p.s, v, 0, &seg)) return;
+  UnitLoads<C> u;
+  unit_loads<C>(p, seg, wave, lane, u);
+#pragma unroll
+  for (int j = 0; j < C::LOADS; ++j)
+    issue_one<C>(j, smem, u.op, u.ma, u.mb, wave, u.k_begin * C::BK);
+  bool stores_behind = false;
+
+  for (int n = 0;; ++n) {
+    typename C::acc_t acc[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) acc[i][j] = typename C::acc_t{};
+
+    if (stores_behind)
+      wait_vm<kStores>();
+    else
+      wait_vm<0>();
+    phase_barrier();
+    if (late) phase_barrier();  // group 1 starts one phase behind
+
+    Frags<C> fr;
+    for (int it = 0; it < u.nk; ++it) {
+      const char* stage = smem + (it & 1) * C::STAGE_BYTES;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        // Memory phase.
+        read_frags<C>(stage, ks, wm, wn, lane, fr);
+        if (ks == 0) {
+          if (it + 1 < u.nk) {
+            const int k0 = (u.k_begin + it + 1) * C::BK;
+#pragma unroll
+            for (int j = 0; j < C::LOADS; ++j)
+              issue_one<C>(j, smem + ((it & 1) ^ 1) * C::STAGE_BYTES, u.op, u.ma, u.mb, wave, k0);
+          }
+        } else {
+          wait_vm<0>();
+        }
+        wait_lgkm_zero();
+        phase_barrier();
+        // Compute phase (serpentine order, as in gemm_pingpong_kernel).
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int jj = 0; jj < C::FN; ++jj) {
+            const int j = (i & 1) ? C::FN - 1 - jj : jj;
+            acc[i][j] = C::M::mma(fr.b[j], fr.a[i], acc[i][j]);
+          }
+        phase_barrier();
+      }
+    }
+
+    // Group 0 is here while group 1 runs its last compute phase: no wave
+    // reads LDS any more, so the next unit's first stage can go out.
+    const Segment done = seg;
+    const int m_base = u.m0 + wm * C::WM;
+    const int n_base = u.n0 + wn * C::WN;
+    const bool more = seg_at_uniform(p.s, v, n + 1, &seg);
+    if (more) {
+      wait_vm<0>();
+      unit_loads<C>(p, seg, wave, lane, u);
+#pragma unroll
+      for (int j = 0; j < C::LOADS; ++j)
+        issue_one<C>(j, smem, u.op, u.ma, u.mb, wave, u.k_begin * C::BK);
+    }
+    if (done.role == ROLE_ONLY) {
+      stores_behind = more && epilogue_vector<C>(p, m_base, n_base);
+      epilogue_stream<C>(p, acc, m_base, n_base, lane);
+    } else {
+      stores_behind = more;
+      write_partial<C>(p.partials + ((int64_t)(done.tile - p.s.shared_base) * p.s.slots + done.index) *
+                                        (C::BM * C::BN / 4),
+                       acc, wave, lane);
+    }
+    // Matches group 1's extra barrier at the start of the unit.
+    if (!late) phase_barrier();
+    if (!more) break;
+  }
+}
+
 // Shares of output tile t under schedule s (1: the tile was stored directly).
 __device__ __forceinline__ int tile_shares(const Sched& s, int t) {
   if (s.mode == MODE_SPLIT) return s.splits;
@@ -1060,12 +1176,14 @@ constexpr KernelInfo kInfos[KID_COUNT] = {
     info_of<K29>("256x128x32_s5_w8_m16_pp"),
     info_of<K30>("64x64x64_s8_w4_m16"),      info_of<K31>("64x64x32_s10_w4_m16"),
     info_of<K32>("128x64x64_s6_w4_m16"),     info_of<K33>("64x64x64_s8_w4"),
-    info_of<K34>("128x128x64_s4_w4_m16_rs"),
+    info_of<K34>("128x128x64_s4_w4_m16_rs"), info_of<K35>("256x256x64_s2_w8_m16_pp"),
 };
 
 template <class C>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t stream) {
-  if constexpr (C::PP)
+  if constexpr (C::PP == 2)
+    hipLaunchKernelGGL(gemm_pingpong64_kernel<C>, dim3(p.s.grid), dim3(C::THREADS), 0, stream, p);
+  else if constexpr (C::PP)
     hipLaunchKernelGGL(gemm_pingpong_kernel<C>, dim3(p.s.grid), dim3(C::THREADS), 0, stream, p);
   else
     hipLaunchKernelGGL(gemm_tiled_kernel<C>, dim3(p.s.grid), dim3(C::THREADS), 0, stream, p);
@@ -1087,7 +1205,9 @@ template <class C>
 int32_t occupancy_cfg() {
   int n = 0;
   hipError_t e;
-  if constexpr (C::PP)
+  if constexpr (C::PP == 2)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_pingpong64_kernel<C>, C::THREADS, 0);
+  else if constexpr (C::PP)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_pingpong_kernel<C>, C::THREADS, 0);
   else
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_tiled_kernel<C>, C::THREADS, 0);

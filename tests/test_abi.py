@@ -275,6 +275,22 @@ def test_default_tail_rule(lib, M, N, K, mode):
     assert check_schedule(rows.tolist(), k_iters, tiles) == []
 
 
+@pytest.mark.parametrize("M,N,K,kid", [
+    (8192, 8192, 8192, 35),     # 4 tiles per CU, K = 8192: 64-wide stages
+    (16384, 16384, 16384, 35),
+    (8192, 8192, 4096, 27),     # K below 8192
+    (4096, 4096, 8192, 27),     # one tile per CU
+    (4608, 4608, 8192, 27),     # tiles left shared by stream-K
+    (2048, 2048, 16384, 27),    # split-K
+])
+def test_default_main_loop(lib, M, N, K, kid):
+    """Two or more 256x256 tiles per CU with K >= 8192 and no shared tail take
+    the main loop over 64-wide stages; other large shapes the 32-wide ring."""
+    assert f"kid={kid} " in gemm.gemm_f16_f32_abt_describe(M, N, K)
+    rows, k_iters, tiles = gemm.gemm_f16_schedule_dump(M, N, K)
+    assert check_schedule(rows.tolist(), k_iters, tiles) == []
+
+
 def test_plan_override_parsed_on_many_threads(lib, monkeypatch):
     """The override is parsed on every plan; ctypes releases the GIL, so
     these calls run concurrently and every one must see the same plan."""
@@ -309,7 +325,7 @@ def test_schedule_model_random_stream_k_plans(lib, monkeypatch):
     for _ in range(300):
         M, N = int(rng.integers(1, 3000)), int(rng.integers(1, 3000))
         K = int(rng.integers(1, 375)) * 8
-        kid = int(rng.choice([0, 4, 6, 16, 18, 25, 26, 27, 29, 33]))
+        kid = int(rng.choice([0, 4, 6, 16, 18, 25, 26, 27, 29, 33, 35]))
         plan = f"kid={kid},mode={int(rng.choice([2, 3]))},grid={int(rng.integers(1, 300))}"
         monkeypatch.setenv("GEMM_F16_PLAN", plan)
         rows, k_iters, tiles = gemm.gemm_f16_schedule_dump(M, N, K)

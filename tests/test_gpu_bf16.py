@@ -169,7 +169,8 @@ def test_k_zero_writes_zeros():
 
 PLANS = ["kid=16", "kid=18", "kid=25", "kid=26", "kid=27", "kid=27,grid=3", "kid=25,grid=2",
          "kid=27,mode=1,splits=3", "kid=26,mode=2,grid=37", "kid=16,mode=1,splits=2",
-         "kid=18,mode=2,grid=29",
+         "kid=18,mode=2,grid=29", "kid=35", "kid=35,grid=3", "kid=35,mode=1,splits=3",
+         "kid=35,mode=3,grid=4",
          # a kernel id not built for bfloat16: the plan keeps the shape rule's kernel
          "kid=0"]
 

@@ -339,8 +339,8 @@ def test_subnormal_inputs():
 
 # Tiled kernel ids 0-9 use v_mfma_f32_32x32x16_f16, 10-24 v_mfma_f32_16x16x32_f16;
 # 25-29 run the ping-pong main loop (28 with the 32x32x16 MFMA); 30-34 are
-# small tiles with deep rings.
-PLANS = [f"kid={k}" for k in range(35)] + [
+# small tiles with deep rings; 35 is the ping-pong loop over two 64-wide stages.
+PLANS = [f"kid={k}" for k in range(36)] + [
     "kid=0,mode=1,splits=3", "kid=0,mode=2", "kid=0,mode=2,grid=37",
     "kid=4,mode=2,grid=100", "kid=6,mode=1,splits=5", "kid=2,mode=2,grid=64",
     "kid=1,mode=1,splits=2", "kid=3,mode=2,grid=29", "kid=5,mode=2,grid=130",
@@ -357,10 +357,13 @@ PLANS = [f"kid={k}" for k in range(35)] + [
     # stores left in flight) with ragged ones (element stores).
     "kid=25,grid=2", "kid=26,grid=3", "kid=27,grid=3", "kid=27,grid=1",
     "kid=27,mode=1,splits=2,grid=7", "kid=28,grid=4", "kid=29,grid=5",
+    "kid=35,grid=1", "kid=35,grid=3", "kid=35,mode=1,splits=2,grid=7", "kid=35,mode=1,splits=3",
+    "kid=35,mode=2", "kid=35,mode=2,grid=37",
     # Whole data-parallel rounds, then stream-K over the tiles left (the
     # forced grids make whole rounds at this size).
     "kid=27,mode=3,grid=4", "kid=26,mode=3,grid=5", "kid=16,mode=3,grid=7",
     "kid=18,mode=3,grid=50", "kid=4,mode=3,grid=11", "kid=29,mode=3,grid=8",
+    "kid=35,mode=3,grid=4",
 ]
 
 
@@ -379,7 +382,7 @@ def test_forced_plans(plan, monkeypatch):
     assert_tol(run(A, B), ref, S, f"{plan} uniform")
 
 
-@pytest.mark.parametrize("kid", [0, 7, 10, 11, 12, 19, 20, 22, 23, 25, 27, 29, 30, 31])
+@pytest.mark.parametrize("kid", [0, 7, 10, 11, 12, 19, 20, 22, 23, 25, 27, 29, 30, 31, 35])
 @pytest.mark.parametrize("K", [24, 72, 200])
 def test_forced_plans_short_k(kid, K, monkeypatch):
     """K of one to a few k-tiles, odd and even counts (one k-step per stage
@@ -395,7 +398,8 @@ def test_forced_plans_short_k(kid, K, monkeypatch):
 
 
 @pytest.mark.parametrize("plan", ["kid=25,grid=1", "kid=26,grid=2", "kid=27,grid=1",
-                                  "kid=27,mode=1,splits=2,grid=3"])
+                                  "kid=27,mode=1,splits=2,grid=3", "kid=35,grid=1",
+                                  "kid=35,grid=2", "kid=35,mode=1,splits=2,grid=3"])
 @pytest.mark.parametrize("K", [24, 72, 200])
 def test_forced_plans_short_units(plan, K, monkeypatch):
     """Many short units per workgroup: units of one to a few k-tiles follow

@@ -30,8 +30,8 @@ from dense_fp16_gemm_03_amd import gemm  # noqa: E402
 DEV = torch.device("cuda:0")
 SEED = 20261202
 N_CASES = 200
-KIDS_F16 = 35
-KIDS_BF16 = (16, 18, 25, 26, 27)
+KIDS_F16 = 36
+KIDS_BF16 = (16, 18, 25, 26, 27, 35)
 
 
 def draw(i):
