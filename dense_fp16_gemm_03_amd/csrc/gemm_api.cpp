@@ -28,7 +28,7 @@ constexpr int64_t kMaxDim = 0x7FFFFFFF - 1024;
 // two waves per SIMD in the ping-pong main loop.
 constexpr int32_t KID_LARGE = KID_256x256x32_S3_W8_M16_PP;
 // The same tiles over two 64-wide stages (whole 128-byte rows per load): for
-// several rounds of tiles with long K.
+// at least a round of tiles with K >= 4096.
 constexpr int32_t KID_LARGE64 = KID_256x256x64_S2_W8_M16_PP;
 
 // Whether the tiles left after whole data-parallel rounds of 256x256 tiles
@@ -147,8 +147,8 @@ bool tiled_eligible(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
 // ring depth and how K is divided; this is the same kind of rule for 256 CUs,
 // set from measurements on the MI355X:
 //   * at least one 256x256 tile per CU: 256x256 tiles, data-parallel,
-//     persistent grid walking the tiles by stride; with two or more tiles per
-//     CU and K >= 8192, the main loop over 64-wide stages;
+//     persistent grid walking the tiles by stride; with K >= 4096 the main
+//     loop over 64-wide stages;
 //   * fewer tiles but long K (>= 128 k-steps of 32): the same tiles with K
 //     split so tiles x splits fills the CUs (each share keeps >= 64 k-steps);
 //   * smaller problems: 128x128 tiles, or 64x64 tiles when 128x128 ones
@@ -227,8 +227,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
     const int64_t t256 = cdiv(M, 256) * cdiv(N, 256);
     const int64_t k32 = cdiv(K, 32);
     if (t256 >= cus) {
-      kid = t256 >= 2 * cus && k32 >= 256 && !share_last_round(t256, k32, cus) ? KID_LARGE64
-                                                                              : KID_LARGE;
+      kid = k32 >= 128 ? KID_LARGE64 : KID_LARGE;
     } else if (k32 >= 128) {
       kid = KID_LARGE;
       int64_t sp = cus / t256;
@@ -266,7 +265,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
   // tiles and the reduce pass cost about 40 us, an idle CU about 0.85 us per
   // k-iteration of 32, so sharing pays from (idle CUs / CUs) * k-iterations
   // of about 44.
-  if (o.mode < 0 && mode == MODE_DATA_PARALLEL && kid == KID_LARGE &&
+  if (o.mode < 0 && mode == MODE_DATA_PARALLEL && (kid == KID_LARGE || kid == KID_LARGE64) &&
       share_last_round(tiles, cdiv(K, 32), cus))
     mode = MODE_DP_SK;
   s.group_m = o.group > 0 ? o.group : 4;

@@ -275,18 +275,22 @@ def test_default_tail_rule(lib, M, N, K, mode):
     assert check_schedule(rows.tolist(), k_iters, tiles) == []
 
 
-@pytest.mark.parametrize("M,N,K,kid", [
-    (8192, 8192, 8192, 35),     # 4 tiles per CU, K = 8192: 64-wide stages
-    (16384, 16384, 16384, 35),
-    (8192, 8192, 4096, 27),     # K below 8192
-    (4096, 4096, 8192, 27),     # one tile per CU
-    (4608, 4608, 8192, 27),     # tiles left shared by stream-K
-    (2048, 2048, 16384, 27),    # split-K
+@pytest.mark.parametrize("M,N,K,kid,mode", [
+    (8192, 8192, 8192, 35, "data_parallel"),   # 4 tiles per CU: 64-wide stages
+    (16384, 16384, 16384, 35, "data_parallel"),
+    (8192, 8192, 4096, 35, "data_parallel"),
+    (4096, 4096, 4096, 35, "data_parallel"),   # one round exactly
+    (4608, 4608, 8192, 35, "dp_stream_k"),     # tiles left shared by stream-K
+    (4096, 4096, 1024, 27, "data_parallel"),   # K below 4096: 32-wide ring
+    (10240, 10240, 2048, 27, "dp_stream_k"),
+    (2048, 2048, 16384, 27, "split"),          # fewer tiles than CUs: split-K
 ])
-def test_default_main_loop(lib, M, N, K, kid):
-    """Two or more 256x256 tiles per CU with K >= 8192 and no shared tail take
-    the main loop over 64-wide stages; other large shapes the 32-wide ring."""
-    assert f"kid={kid} " in gemm.gemm_f16_f32_abt_describe(M, N, K)
+def test_default_main_loop(lib, M, N, K, kid, mode):
+    """At least a round of 256x256 tiles with K >= 4096 takes the main loop
+    over 64-wide stages (whether or not the tiles left are shared); shorter K
+    and split plans keep the 32-wide ring."""
+    text = gemm.gemm_f16_f32_abt_describe(M, N, K)
+    assert f"kid={kid} " in text and f"mode={mode} " in text
     rows, k_iters, tiles = gemm.gemm_f16_schedule_dump(M, N, K)
     assert check_schedule(rows.tolist(), k_iters, tiles) == []
 
