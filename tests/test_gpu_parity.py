@@ -190,6 +190,23 @@ def test_default_rounds_then_stream_k(M, N, K):
     assert np.all(got == float(w.sum())), f"k-block sum: got {np.unique(got)[:5]}"
 
 
+@pytest.mark.parametrize("M,N,K", [(4100, 4150, 4104), (8200, 8000, 8200)])
+def test_default_large_ragged(M, N, K):
+    """Large shapes with ragged M, N and K on the default plan (64-wide stages,
+    the tiles past whole rounds shared by stream-K, a partial last k-stage):
+    integers bit-exact on sampled rows, columns and points, including the
+    last row and column."""
+    text = gemm.gemm_f16_f32_abt_describe(M, N, K)
+    log(f"  plan: {text}")
+    assert "kid=35" in text
+    A, B = inputs.integer(M, K, 171), inputs.integer(N, K, 172)
+    got = run(A, B)
+    assert np.isfinite(got).all(), "C not fully written"
+    rows, cols = sample_points(M, N, n_rand=2000)
+    ref, _ = oracle.gemm_abt_elems(A, B, rows, cols)
+    assert_exact(got[rows, cols], ref, f"{M}x{N}x{K} integer")
+
+
 def test_hash_int_inputs():
     """Integers in [-3, 3] from a hash of the index: exact."""
     M, N, K = 1024, 1024, 4096
