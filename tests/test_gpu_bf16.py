@@ -57,9 +57,10 @@ def sample_points(M, N, n_rand=2000, seed=0):
     rng = np.random.default_rng(seed)
     rows = [0, M - 1, M // 2, 257 % M]
     cols = [0, N - 1, N // 2, 259 % N]
-    r = np.concatenate([np.repeat(rows, N), np.tile(np.arange(N), len(rows)),
+    # whole rows `rows`, whole columns `cols`, then random points
+    r = np.concatenate([np.repeat(rows, N), np.tile(np.arange(M), len(cols)),
                         rng.integers(0, M, n_rand)])
-    c = np.concatenate([np.tile(np.arange(N), len(rows)), np.repeat(cols, N)[:N * len(rows)],
+    c = np.concatenate([np.tile(np.arange(N), len(rows)), np.repeat(cols, M),
                         rng.integers(0, N, n_rand)])
     return r, c
 
@@ -125,6 +126,20 @@ def test_kblock_weighted_ones(name):
     B = np.broadcast_to(inputs.to_bf16_bits(w), (N, K)).copy()
     got = run(inputs.to_bf16_bits(np.ones((M, K))), B)
     assert np.all(got == float(w.sum()))
+
+
+@pytest.mark.parametrize("M,N,K", [(4352, 4352, 4096), (4100, 4150, 4104)])
+def test_default_rounds_then_stream_k(M, N, K):
+    """bfloat16 on the default plans that share the tiles left after whole
+    data-parallel rounds (64-wide stages; the second shape ragged in M, N
+    and K): integers bit-exact, uniform within tolerance, on sampled points."""
+    text = gemm.gemm_f16_f32_abt_describe(M, N, K)
+    log(f"  plan: {text}")
+    assert "mode=dp_stream_k" in text and "kid=35" in text
+    A, B = inputs.integer_bf16(M, K, 191), inputs.integer_bf16(N, K, 192)
+    check(A, B, run(A, B), "integer", f"{M}x{N}x{K} bf16 integer", sampled=True)
+    A, B = inputs.uniform_bf16(M, K, 193), inputs.uniform_bf16(N, K, 194)
+    check(A, B, run(A, B), "uniform", f"{M}x{N}x{K} bf16 uniform", sampled=True)
 
 
 @pytest.mark.parametrize("M,N,K", [(600, 520, 1352), (1, 1, 8), (129, 77, 200),
