@@ -2,35 +2,44 @@
 """Benchmark of C = A * B^T (fp16 in, fp32 accumulate/out) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8192^3] [--dtype f16|bf16]
-                    [--no-cpu-baseline] [--no-extras] [--shapes] [--vendor] [--calibrate-copy]
+                    [--inputs uniform|hash_int|integer] [--no-cpu-baseline] [--no-extras]
+                    [--sweeps S] [--page-shapes] [--vendor] [--calibrate-copy]
 
 A step is one call of gemm_f16_f32_abt through the C ABI on synthetic
 operands already resident in HBM (uniform [-1, 1] fp16, seeds 1 and 2). The
 timed region is K back-to-back calls bracketed by device synchronisation;
 `value` is 2*M*N*K*K / elapsed in TFLOP/s. Each call is also bracketed by HIP
-events on the launch stream: their mean is the kernel's average launch
-duration, from which `roofline.achieved` is computed against the fp16 MFMA
-peak (2.5 PFLOP/s dense).
+events on the launch stream: their mean, median and minimum are the kernel's
+launch durations, from which `roofline.achieved` is computed against the fp16
+MFMA peak (2.5 PFLOP/s dense).
 
-At 8192^3 the line also carries `long_k`: the two long-K workloads, 200
-back-to-back calls after 100 untimed ones, between one pair of HIP events
-(their main and reduce kernels and the gaps between calls), as fractions of
-peak beside the headline; and `pages_inputs`: 8192^3 again on the input kind
-the pages time on (integers in [-3, 3] from a hash), which draws less power
-on this board. `--no-extras` leaves both out. The default 30
-warm-up calls of the headline, and the 100 here, let the board's clocks
-settle: the first 20 or so calls of a new shape run several percent slower.
+Clock: the library's clock probe (gemm_f16_set_clock_probe) is on during the
+timed calls: the first wave of workgroup 0 of every main-kernel launch adds
+its shader-clock cycles and 100 MHz real-time ticks to two counters, so
+`roofline.sclk_mhz` is the average shader clock while the timed kernels ran
+and `roofline.frac_at_sclk` the fraction of the peak at that clock. The
+board's own telemetry (amdsmi gpu_metrics: gfx clocks, socket power, time at
+the package power limit) updates too slowly for a window of a few
+milliseconds, so `sustained` runs the headline call back to back for about two
+seconds after everything else and reports the probe clock, the per-call time
+and the board's power and power-limit residency over that loop.
 
-With --shapes, per-shape lines (`shapes`) time the five workloads the way "SASS-Level Kernel
+`configs` (unless --no-extras): the five workloads the way "SASS-Level Kernel
 Generation for Blackwell" measures (section "How we measured"): every call
-runs alone (synchronised after each), the time of a call is its GPU time, and
-the median over the last N calls is reported, over sweeps run in forward then
-reverse order.
+runs alone and the time of a call is its GPU time; the median over the last N
+calls is reported, over sweeps run in forward then reverse order. A short
+spin kernel is queued ahead of each timed call so that the call's events and
+kernels reach the GPU together: the events then bracket the call's kernels
+(and the gaps between them), not the host's launch latency. Beside it, the
+same calls back to back (one pair of events around N calls) and the host time
+to issue one call through the Python binding. Each config carries its own
+roofline: MFMA for the compute-bound shapes, HBM for those below the ridge.
+`pages_inputs`: the headline shape on the input kind the pages time on
+(integers in [-3, 3] from a hash), which draws less power on this board.
 
 `cpu_baseline` times the CPU reference (oracle/) on a bounded sample of the
 same workload: whole rows of C, sized from a first timing to about 25 s (in
-practice 10-20 s) on the host's
-cores.
+practice 10-20 s) on the host's cores.
 """
 from __future__ import annotations
 
@@ -39,6 +48,7 @@ import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 import numpy as np
@@ -49,6 +59,7 @@ sys.path.insert(0, ROOT)
 METRIC = ("TFLOP/s and µs/call per M×N×K (fp16→fp32 A·Bᵀ); "
           "% of MI355X MFMA peak")
 PEAK_TFLOPS = 2500.0         # MI355X dense fp16 MFMA (published)
+PEAK_SCLK_MHZ = 2400.0       # the clock the published peak assumes
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E (published)
 # The pages' own numbers (one B200, "SASS-Level Kernel Generation for Blackwell",
 # section "The numbers"): midpoints of the ranges, in us per call. Context only.
@@ -83,11 +94,19 @@ def algorithmic(M, N, K):
     return flops, nbytes
 
 
-def make_device_operands(torch, shape, dev, dtype="f16"):
+def roofline_time(M, N, K):
+    """(seconds at the roofline, bound) for one call of the shape."""
+    f, b = algorithmic(M, N, K)
+    t_mfma = f / (PEAK_TFLOPS * 1e12)
+    t_hbm = b / (HBM_PEAK_GBS * 1e9)
+    return (t_mfma, "mfma") if t_mfma >= t_hbm else (t_hbm, "hbm")
+
+
+def make_device_operands(torch, shape, dev, dtype="f16", kind="uniform"):
     """Host operands (float16, or uint16 bfloat16 bits) and their device copies."""
     from dense_fp16_gemm_03_amd import inputs
 
-    A, B = inputs.workload_operands(shape, "uniform", dtype)
+    A, B = inputs.workload_operands(shape, kind, dtype)
     if dtype == "bf16":
         def dev_t(x):
             return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -97,56 +116,298 @@ def make_device_operands(torch, shape, dev, dtype="f16"):
     return A, B, dev_t(A), dev_t(B)
 
 
-def time_throughput(torch, gemm, At, Bt, C, steps, warmup):
+class ClockSampler:
+    """Board telemetry sampled by a thread through amdsmi (in-process, no
+    child): per-XCD gfx clocks, socket power, and the accumulated time at
+    the package power limit (PPT) and energy. `window(t0, t1)` summarises
+    the samples taken between two perf_counter() instants. Optional: if
+    amdsmi is unavailable, every summary is None."""
+
+    def __init__(self):
+        self.samples = []  # (t, [gfx MHz per XCD], socket W, ppt_acc, acc_counter, energy)
+        self.ok = False
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            self._read()  # one read to see that it works
+            self.samples.clear()
+            self.ok = True
+        except Exception as e:  # noqa: BLE001 - telemetry is optional context
+            log(f"[bench] no telemetry: {type(e).__name__}: {e}")
+
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        clks = [c for c in m.get("current_gfxclks", []) if isinstance(c, int) and 0 < c < 10000]
+
+        def num(key):
+            v = m.get(key)
+            return v if isinstance(v, (int, float)) else None
+
+        self.samples.append((time.perf_counter(), clks, num("current_socket_power"),
+                             num("ppt_residency_acc"), num("accumulation_counter"),
+                             num("energy_accumulator")))
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                self._read()
+            except Exception:  # noqa: BLE001
+                return
+            time.sleep(0.0005)
+
+    def start(self):
+        if self.ok and self._thread is None:
+            self._thread = threading.Thread(target=self._loop, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join(timeout=5)
+            self._thread = None
+
+    def window(self, t0, t1):
+        """Summary of the samples taken in [t0, t1] (None if there are none)."""
+        inside = [s for s in self.samples if t0 <= s[0] <= t1 and s[1]]
+        if not inside:
+            return None
+        per_xcd = np.array([s[1] for s in inside if len(s[1]) == len(inside[0][1])], float)
+        out = {"samples": len(inside),
+               "gfx_clk_mhz_mean": round(float(per_xcd.mean()), 1),
+               "gfx_clk_mhz_per_xcd": [round(float(v), 1) for v in per_xcd.mean(axis=0)],
+               "gfx_clk_mhz_min": round(float(per_xcd.min()), 1),
+               "gfx_clk_mhz_max": round(float(per_xcd.max()), 1)}
+        pw = [s[2] for s in inside if s[2] is not None]
+        if pw:
+            out["socket_power_w_mean"] = round(float(np.mean(pw)), 1)
+            out["socket_power_w_max"] = float(max(pw))
+        # time at the power limit: residency counter over the accumulation
+        # counter, between the first and last sample of the window
+        a, b = inside[0], inside[-1]
+        if None not in (a[3], b[3], a[4], b[4]) and b[4] > a[4]:
+            out["ppt_limited_frac"] = round((b[3] - a[3]) / (b[4] - a[4]), 3)
+        out["source"] = "amdsmi gpu_metrics, sampled in-process during the calls"
+        return out
+
+
+class Probe:
+    """The library's clock probe over a region of calls: counters on the
+    device, zeroed in stream order before the region, read after it."""
+
+    def __init__(self, torch, gemm, dev):
+        self.torch, self.gemm = torch, gemm
+        self.ctr = torch.zeros(2, dtype=torch.int64, device=dev)
+
+    def __enter__(self):
+        self.ctr.zero_()
+        self.gemm.gemm_f16_set_clock_probe(self.ctr.data_ptr())
+        return self
+
+    def __exit__(self, *exc):
+        self.gemm.gemm_f16_set_clock_probe(0)
+
+    def mhz(self):
+        """Average shader clock (MHz) of the probed launches (after a sync)."""
+        self.torch.cuda.synchronize()
+        cycles, ticks = (int(v) for v in self.ctr.tolist())
+        return round(100.0 * cycles / ticks, 1) if ticks > 0 else None
+
+
+def time_headline(torch, gemm, At, Bt, C, steps, warmup, probe):
+    """Warm-up, then `steps` back-to-back calls bracketed by synchronisation,
+    each also between HIP events on the launch stream; the clock probe is on
+    for the timed calls only."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         gemm.gemm_abt(At, Bt, C, stream=stream)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s, e in ev:
+    with probe:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s, e in ev:
+            s.record(stream)
+            gemm.gemm_abt(At, Bt, C, stream=stream)
+            e.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    kernel_us = [s.elapsed_time(e) * 1e3 for s, e in ev]
+    return t1 - t0, kernel_us, probe.mhz()
+
+
+def sustained(torch, gemm, At, Bt, C, flops, probe, sampler, seconds=2.0):
+    """The headline call back to back for about `seconds`: probe clock and
+    per-call time over the whole loop, board telemetry (amdsmi) over its
+    second half."""
+    stream = torch.cuda.current_stream()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    calls = 0
+    sampler.start()
+    with probe:
+        torch.cuda.synchronize()
         s.record(stream)
-        gemm.gemm_abt(At, Bt, C, stream=stream)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(8):
+                gemm.gemm_abt(At, Bt, C, stream=stream)
+            calls += 8
+            torch.cuda.synchronize()
         e.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    kernel_ms = [s.elapsed_time(e) for s, e in ev]
-    return t1 - t0, kernel_ms
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    sampler.stop()
+    us = s.elapsed_time(e) * 1e3 / calls
+    mhz = probe.mhz()
+    out = {"calls": calls, "us_per_call": round(us, 3),
+           "tflops": round(flops / (us * 1e-6) / 1e12, 2), "sclk_mhz": mhz,
+           "board": sampler.window(t0 + (t1 - t0) / 2, t1)}
+    if mhz:
+        out["frac_at_sclk"] = round(flops / (us * 1e-6) / 1e12
+                                    / (PEAK_TFLOPS * mhz / PEAK_SCLK_MHZ), 4)
+    return out
 
 
-def time_loop(torch, gemm, At, Bt, C, calls, warmup):
-    """Microseconds per call over `calls` back-to-back calls, from one pair of
-    HIP events around the whole loop (no event between calls)."""
+class Spinner:
+    """A spin kernel of a calibrated length (about `us` microseconds), queued
+    ahead of a call timed alone so that the call's start event, kernels and
+    end event are all in the queue before the GPU reaches them."""
+
+    def __init__(self, torch, us=150.0):
+        self.torch = torch
+        self.cycles = 0
+        self.us = None
+        stream = torch.cuda.current_stream()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+        def took(cycles):
+            torch.cuda._sleep(cycles)
+            s.record(stream)
+            torch.cuda._sleep(cycles)
+            e.record(stream)
+            e.synchronize()
+            return s.elapsed_time(e) * 1e3
+
+        cycles = 20000
+        for _ in range(4):
+            t = took(cycles)
+            if t < 1.0:  # no measurable spin: grow by a bounded step
+                cycles *= 10
+            else:
+                cycles = int(cycles * min(max(us / t, 0.1), 10.0))
+            cycles = min(cycles, 50_000_000)
+        t = took(cycles)
+        if us / 3 <= t <= us * 3:
+            self.cycles, self.us = cycles, round(t, 1)
+        else:
+            log(f"[bench] spin kernel not calibrated ({cycles} cycles took {t:.1f} us): "
+                "calls alone are timed without it (their times include the launch latency)")
+
+    def __call__(self):
+        if self.cycles:
+            self.torch.cuda._sleep(self.cycles)
+
+
+def time_calls_alone(torch, fn, calls, warmup, spinner):
+    """GPU time (us) of each of `calls` calls of fn(), every call alone."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
-        gemm.gemm_abt(At, Bt, C, stream=stream)
+        fn()
+    torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    s.record(stream)
-    for _ in range(calls):
-        gemm.gemm_abt(At, Bt, C, stream=stream)
-    e.record(stream)
-    e.synchronize()
-    return s.elapsed_time(e) * 1e3 / calls
-
-
-def time_calls_alone(torch, gemm, At, Bt, C, calls, warmup=20):
-    """Median GPU time of a call when every call runs alone."""
-    stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        gemm.gemm_abt(At, Bt, C, stream=stream)
-    torch.cuda.synchronize()
     out = []
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for _ in range(calls):
+        spinner()
         s.record(stream)
-        gemm.gemm_abt(At, Bt, C, stream=stream)
+        fn()
         e.record(stream)
         e.synchronize()
         out.append(s.elapsed_time(e) * 1e3)
-    out.sort()
-    return out[len(out) // 2]
+    return out
+
+
+def time_back_to_back(torch, fn, calls, warmup):
+    """(GPU us per call over `calls` back-to-back calls between one pair of
+    events, host us to issue one call)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record(stream)
+    h0 = time.perf_counter()
+    for _ in range(calls):
+        fn()
+    h1 = time.perf_counter()
+    e.record(stream)
+    e.synchronize()
+    return s.elapsed_time(e) * 1e3 / calls, (h1 - h0) * 1e6 / calls
+
+
+def measure_configs(torch, gemm, table, dev, dtype, sweeps, spinner, cache, probe):
+    """Per-config lines: calls alone (median, min, max over sweeps, and the
+    probe clock over them), back to back, host issue time, roofline
+    fraction."""
+    names = list(table)
+    alone = {n: [] for n in names}
+    clocks = {n: [] for n in names}
+    for sweep in range(sweeps):
+        order = names if sweep % 2 == 0 else names[::-1]
+        for n in order:
+            m, nn, k = table[n]
+            if n not in cache:
+                _, _, a, b = make_device_operands(torch, (m, nn, k), dev, dtype)
+                c = torch.empty((m, nn), dtype=torch.float32, device=dev)
+                cache[n] = (a, b, c)
+            a, b, c = cache[n]
+            for _ in range(20):
+                gemm.gemm_abt(a, b, c)
+            with probe:
+                us = time_calls_alone(torch, lambda: gemm.gemm_abt(a, b, c), CALLS[n], 0,
+                                      spinner)
+            clocks[n].append(probe.mhz())
+            alone[n].append(us)
+            log(f"[bench] sweep {sweep} {n}: median {float(np.median(us)):.2f} us/call alone")
+    out = []
+    for n in names:
+        m, nn, k = table[n]
+        a, b, c = cache[n]
+        b2b_us, host_us = time_back_to_back(torch, lambda: gemm.gemm_abt(a, b, c),
+                                            CALLS[n], 50)
+        f, by = algorithmic(m, nn, k)
+        t_roof, bound = roofline_time(m, nn, k)
+        meds = [float(np.median(x)) for x in alone[n]]
+        allv = np.concatenate([np.asarray(x) for x in alone[n]])
+        med = float(np.median(meds))
+        entry = {"workload": n, "M": m, "N": nn, "K": k,
+                 "us_per_call_alone": {"median": round(med, 3),
+                                       "sweep_medians": [round(v, 3) for v in meds],
+                                       "min": round(float(allv.min()), 3),
+                                       "max": round(float(allv.max()), 3),
+                                       "calls_per_sweep": CALLS[n], "sweeps": len(meds)},
+                 "us_per_call_back_to_back": round(b2b_us, 3),
+                 "host_us_per_call": round(host_us, 2),
+                 "tflops": round(f / (med * 1e-6) / 1e12, 2),
+                 "roofline": {"bound": bound, "t_roof_us": round(t_roof * 1e6, 3),
+                              "frac": round(t_roof / (med * 1e-6), 4)},
+                 "mfma_peak_frac": round(f / (med * 1e-6) / 1e12 / PEAK_TFLOPS, 4),
+                 "plan": gemm.gemm_f16_f32_abt_describe(m, nn, k)}
+        mhz = [c for c in clocks[n] if c]
+        if mhz:
+            entry["sclk_mhz"] = round(float(np.mean(mhz)), 1)
+            if bound == "mfma":
+                entry["frac_at_sclk"] = round(entry["mfma_peak_frac"] * PEAK_SCLK_MHZ
+                                              / entry["sclk_mhz"], 4)
+        if n in PAGE_US and dtype == "f16":
+            entry["pages_b200_us"] = round(PAGE_US[n], 3)
+        log(f"[bench] {n}: alone {med:.2f} us ({entry['roofline']['frac'] * 100:.1f}% of its "
+            f"{bound} roofline), back to back {b2b_us:.2f} us, host {host_us:.2f} us/call")
+        out.append(entry)
+    return out
 
 
 def cpu_baseline(A, B, M, N, K, budget_s=25.0):
@@ -170,35 +431,14 @@ def cpu_baseline(A, B, M, N, K, budget_s=25.0):
                       f"binary64 triple loop on {threads} threads"}
 
 
-def _time_alone(torch, fn, calls, warmup=5):
-    """Median GPU time (us) of fn() when every call runs alone."""
-    stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    out = []
-    for _ in range(calls):
-        s.record(stream)
-        fn()
-        e.record(stream)
-        e.synchronize()
-        out.append(s.elapsed_time(e) * 1e3)
-    out.sort()
-    return out[len(out) // 2]
+def _median_alone(torch, fn, calls, spinner, warmup=5):
+    return float(np.median(time_calls_alone(torch, fn, calls, warmup, spinner)))
 
 
-def vendor_arm(torch, gemm, names, dev):
-    """hipBLASLt context arm ("How we measured" in "SASS-Level Kernel
-    Generation for Blackwell"): every algorithm of the vendor heuristic is run
-    on hash-integer inputs, where any summation order is exact, and kept only
-    if its C equals ours bit for bit; the fastest kept one is then timed
-    against ours, calls alone, in the order ours, vendor, vendor, ours, on
-    both uniform and hash-integer inputs. Context only, never the bench value."""
+def load_vendor():
     import ctypes
 
     from dense_fp16_gemm_03_amd import build as b
-    from dense_fp16_gemm_03_amd import inputs
 
     if not os.path.exists(b.VENDOR_LIBRARY):
         raise RuntimeError(f"{b.VENDOR_LIBRARY} is not built "
@@ -211,59 +451,90 @@ def vendor_arm(torch, gemm, names, dev):
     lib.vendor_hipblaslt_workspace.restype = ctypes.c_size_t
     lib.vendor_hipblaslt_run.argtypes = [i64, p, p, p, p, ctypes.c_size_t, p]
     lib.vendor_hipblaslt_run.restype = ctypes.c_int
+    return lib
+
+
+def vendor_screen(torch, lib, A, B, C_ref, max_algorithms=64):
+    """Runs every algorithm hipBLASLt's heuristic returns for C = A B^T (fp16
+    in, fp32 out) on the device operands A, B and returns (count, workspace,
+    exact): the indices whose C equals C_ref bit for bit. On integer-valued
+    inputs, where every summation order gives the exact C, C_ref is this
+    library's result, whose exactness on such inputs the GPU tests prove
+    against the CPU reference (and the vendor test checks this screen
+    against it directly)."""
+    M, K = A.shape
+    N = B.shape[0]
+    count = lib.vendor_hipblaslt_prepare(M, N, K, K, K, N, max_algorithms)
+    if count <= 0:
+        return int(count), None, []
+    ws_bytes = max(lib.vendor_hipblaslt_workspace(i) for i in range(count))
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=A.device)
+    stream = torch.cuda.current_stream().cuda_stream
+    Cv = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    exact = []
+    for i in range(count):
+        Cv.fill_(float("nan"))
+        st = lib.vendor_hipblaslt_run(i, A.data_ptr(), B.data_ptr(), Cv.data_ptr(),
+                                      ws.data_ptr(), ws.numel(), stream)
+        torch.cuda.synchronize()
+        if st == 0 and torch.equal(Cv, C_ref):
+            exact.append(i)
+    return int(count), ws, exact
+
+
+def vendor_arm(torch, gemm, names, dev, spinner):
+    """hipBLASLt context arm ("How we measured" in "SASS-Level Kernel
+    Generation for Blackwell"): every algorithm of the vendor heuristic is run
+    on hash-integer inputs, where any summation order is exact, and kept only
+    if its C is exact (vendor_screen); the fastest kept one is then timed
+    against ours, calls alone, in the order ours, vendor, vendor, ours, on
+    both uniform and hash-integer inputs. Context only, never the bench value."""
+    from dense_fp16_gemm_03_amd import inputs
+
+    lib = load_vendor()
     out = []
     for n in names:
         M, N, K = inputs.WORKLOADS[n]
-        count = lib.vendor_hipblaslt_prepare(M, N, K, K, K, N, 64)
-        if count <= 0:
-            log(f"[vendor] {n}: heuristic returned {count}")
-            out.append({"workload": n, "algorithms": int(count)})
-            continue
-        ws_bytes = max(lib.vendor_hipblaslt_workspace(i) for i in range(count))
-        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-        stream = torch.cuda.current_stream().cuda_stream
-        Ch = torch.empty((M, N), dtype=torch.float32, device=dev)
-        Cv = torch.empty_like(Ch)
         Ah, Bh = (torch.from_numpy(x).to(dev) for x in inputs.workload_operands((M, N, K),
                                                                                  "hash_int"))
+        Ch = torch.empty((M, N), dtype=torch.float32, device=dev)
         gemm.gemm_abt(Ah, Bh, Ch)
+        torch.cuda.synchronize()
+        count, ws, exact = vendor_screen(torch, lib, Ah, Bh, Ch)
+        if not exact:
+            log(f"[vendor] {n}: {count} algorithms, none exact")
+            out.append({"workload": n, "algorithms": count, "exact": 0})
+            continue
+        stream = torch.cuda.current_stream().cuda_stream
+        Cv = torch.empty_like(Ch)
 
-        def run_vendor(i, A_, B_, C_):
-            st = lib.vendor_hipblaslt_run(i, A_.data_ptr(), B_.data_ptr(), C_.data_ptr(),
+        def run_vendor(i, A_, B_):
+            st = lib.vendor_hipblaslt_run(i, A_.data_ptr(), B_.data_ptr(), Cv.data_ptr(),
                                           ws.data_ptr(), ws.numel(), stream)
             if st != 0:
                 raise RuntimeError(f"hipBLASLt algorithm {i} failed with status {st}")
 
         screen_calls = 10 if M * N * K >= 1 << 36 else 50
-        exact, times = 0, []
-        for i in range(count):
-            Cv.fill_(float("nan"))
-            run_vendor(i, Ah, Bh, Cv)
-            torch.cuda.synchronize()
-            if not torch.equal(Cv, Ch):
-                continue
-            exact += 1
-            times.append((_time_alone(torch, lambda: run_vendor(i, Ah, Bh, Cv), screen_calls), i))
-        if not times:
-            out.append({"workload": n, "algorithms": int(count), "exact": 0})
-            continue
+        times = [(_median_alone(torch, lambda: run_vendor(i, Ah, Bh), screen_calls, spinner), i)
+                 for i in exact]
         best = min(times)[1]
-        entry = {"workload": n, "M": M, "N": N, "K": K, "algorithms": int(count),
-                 "exact": exact, "best_algorithm": best}
+        entry = {"workload": n, "M": M, "N": N, "K": K, "algorithms": count,
+                 "exact": len(exact), "best_algorithm": best}
         for kind, (A_, B_) in (("uniform", make_device_operands(torch, (M, N, K), dev)[2:]),
                                ("hash_int", (Ah, Bh))):
             ours, theirs = [], []
             for who in ("ours", "vendor", "vendor", "ours"):
                 if who == "ours":
-                    ours.append(_time_alone(torch, lambda: gemm.gemm_abt(A_, B_, Ch), CALLS[n]))
+                    ours.append(_median_alone(torch, lambda: gemm.gemm_abt(A_, B_, Ch),
+                                              CALLS[n], spinner))
                 else:
-                    theirs.append(_time_alone(torch, lambda: run_vendor(best, A_, B_, Cv),
-                                              CALLS[n]))
+                    theirs.append(_median_alone(torch, lambda: run_vendor(best, A_, B_),
+                                                CALLS[n], spinner))
             entry[kind] = {"ours_us": [round(min(ours), 3), round(max(ours), 3)],
                            "hipblaslt_us": [round(min(theirs), 3), round(max(theirs), 3)]}
             log(f"[vendor] {n} {kind}: ours {min(ours):.2f}-{max(ours):.2f} us, hipBLASLt "
                 f"{min(theirs):.2f}-{max(theirs):.2f} us (algorithm {best} of {count}, "
-                f"{exact} exact)")
+                f"{len(exact)} exact)")
         out.append(entry)
         del Ah, Bh, Ch, Cv, ws
         torch.cuda.empty_cache()
@@ -283,45 +554,6 @@ def calibrate_copy(torch):
                       "launches": 5}), flush=True)
 
 
-def telemetry(torch, gemm, At, Bt, C, seconds=3.0):
-    """Clock and power while the GEMM runs back to back: amd-smi (a child
-    process) samples the board during a loop of calls. Context for reading the
-    power-limited clock, outside the timed region; None if amd-smi fails."""
-    import shutil
-    import subprocess
-
-    smi = shutil.which("amd-smi")
-    if smi is None:
-        return None
-    stream = torch.cuda.current_stream()
-
-    def burst():
-        for _ in range(8):
-            gemm.gemm_abt(At, Bt, C, stream=stream)
-        torch.cuda.synchronize()
-
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < 1.0:  # reach the loaded clock first
-        burst()
-    proc = subprocess.Popen([smi, "metric", "-g", "0", "--power", "--clock", "--json"],
-                            stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
-    t0 = time.perf_counter()
-    while proc.poll() is None and time.perf_counter() - t0 < seconds:
-        burst()
-    try:
-        out, _ = proc.communicate(timeout=30)
-        d = json.loads(out)
-        gpu = d["gpu_data"][0] if isinstance(d, dict) else d[0]
-        clocks = [v["clk"]["value"] for k, v in gpu["clock"].items()
-                  if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
-        power = gpu["power"]["socket_power"]["value"]
-        return {"gfx_clk_mhz": clocks, "socket_power_w": power,
-                "source": "amd-smi metric --power --clock, sampled during back-to-back calls"}
-    except Exception:  # noqa: BLE001 - telemetry is optional context
-        proc.kill()
-        return None
-
-
 def library_md5() -> str:
     from dense_fp16_gemm_03_amd import gemm
 
@@ -337,7 +569,7 @@ def parse_shape(text):
     return tuple(int(p) for p in parts)
 
 
-def traffic_for(workload, kernel_avg_s):
+def traffic_for(workload):
     """HBM bytes per launch from committed rocprofv3 counters, if they match this source."""
     try:
         with open(TRAFFIC_FILE) as f:
@@ -357,24 +589,25 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--dtype", default="f16", choices=("f16", "bf16"),
                     help="operand type: binary16 (the workloads' type) or bfloat16")
+    ap.add_argument("--inputs", default="uniform", choices=("uniform", "hash_int", "integer"),
+                    help="input kind of the headline calls (the workloads are quoted on "
+                         "uniform; the others are controls for the data-dependent clock)")
     ap.add_argument("--workload", default="8192^3",
                     help="one of the five workloads, one of the pages' other shapes, "
                          "or any MxNxK")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", "--no-long-k", dest="no_extras", action="store_true",
-                    help="at 8192^3, skip the extra rows (the two long-K workloads and the "
-                         "hash-integer inputs); profiling runs use this so their traces hold "
-                         "one shape and one input kind")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the headline calls (no configs table, no hash-integer "
+                         "row); profiling runs use this so their traces hold one shape and "
+                         "one input kind")
     ap.add_argument("--no-telemetry", action="store_true",
-                    help="skip the amd-smi clock/power sample after the timed region")
-    ap.add_argument("--shapes", action="store_true",
-                    help="also time the five workloads, each call alone")
+                    help="skip the sustained loop with the board's telemetry")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB fp32 copy kernel (counter calibration)")
-    ap.add_argument("--sweeps", type=int, default=4,
-                    help="sweeps over the shapes, alternately forward and reverse")
+    ap.add_argument("--sweeps", type=int, default=2,
+                    help="sweeps over the configs, alternately forward and reverse")
     ap.add_argument("--page-shapes", action="store_true",
-                    help="with --shapes, also time the other shapes of the pages' table")
+                    help="also time the other shapes of the pages' table in `configs`")
     ap.add_argument("--vendor", action="store_true",
                     help="also time hipBLASLt's fastest exact algorithm on every workload "
                          "(context only)")
@@ -409,107 +642,85 @@ def main():
     M, N, K = shape
     flops, nbytes = algorithmic(M, N, K)
     log(f"[bench] workload {name}: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
-    A, B, At, Bt = make_device_operands(torch, (M, N, K), dev, args.dtype)
+    A, B, At, Bt = make_device_operands(torch, (M, N, K), dev, args.dtype, args.inputs)
     C = torch.empty((M, N), dtype=torch.float32, device=dev)
 
-    elapsed, kernel_ms = time_throughput(torch, gemm, At, Bt, C, args.steps, args.warmup)
+    probe = Probe(torch, gemm, dev)
+    elapsed, kernel_us, sclk = time_headline(torch, gemm, At, Bt, C, args.steps, args.warmup,
+                                             probe)
     ms_per_step = elapsed / args.steps * 1e3
     value = flops * args.steps / elapsed / 1e12
-    avg_kernel_s = sum(kernel_ms) / len(kernel_ms) / 1e3
-    achieved = flops / avg_kernel_s / 1e12
+    k_mean = float(np.mean(kernel_us))
+    k_med = float(np.median(kernel_us))
+    k_min = float(np.min(kernel_us))
+    achieved = flops / (k_mean * 1e-6) / 1e12
     log(f"[bench] {args.steps} steps in {elapsed * 1e3:.2f} ms: {value:.1f} TFLOP/s; "
-        f"kernel avg {avg_kernel_s * 1e6:.2f} us ({achieved:.1f} TFLOP/s)")
-    # committed counters are for the binary16 path
-    traffic = traffic_for(name, avg_kernel_s) if args.dtype == "f16" else None
+        f"kernel mean {k_mean:.2f} us, median {k_med:.2f}, min {k_min:.2f} "
+        f"({achieved:.1f} TFLOP/s)")
+    # committed counters are for the binary16 path on uniform inputs
+    traffic = traffic_for(name) if (args.dtype == "f16" and args.inputs == "uniform") else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
-                "kernel_avg_us": round(avg_kernel_s * 1e6, 3),
+                "kernel_us": {"mean": round(k_mean, 3), "median": round(k_med, 3),
+                              "min": round(k_min, 3), "calls": len(kernel_us)},
                 "algorithmic_bytes": nbytes, "algorithmic_flops": flops}
+    if sclk:
+        roofline["sclk_mhz"] = sclk
+        roofline["sclk_source"] = "clock probe over the timed launches (workgroup 0)"
+        roofline["peak_at_sclk"] = round(PEAK_TFLOPS * sclk / PEAK_SCLK_MHZ, 1)
+        roofline["frac_at_sclk"] = round(achieved / (PEAK_TFLOPS * sclk / PEAK_SCLK_MHZ), 4)
+        log(f"[bench] shader clock during the timed calls: {sclk} MHz "
+            f"({roofline['frac_at_sclk'] * 100:.1f}% of the peak at that clock)")
 
-    shapes = []
-    if args.shapes:
+    configs, pages_inputs = [], None
+    if not args.no_extras:
+        spinner = Spinner(torch)
         table = dict(inputs.WORKLOADS)
         if args.page_shapes:
             table.update(inputs.PAGE_SHAPES)
-        names = list(table)
-        results = {n: [] for n in names}
-        for sweep in range(args.sweeps):
-            order = names if sweep % 2 == 0 else names[::-1]
-            for n in order:
-                m, nn, k = table[n]
-                if n == name:
-                    a, b = At, Bt
-                    c = C
-                else:
-                    _, _, a, b = make_device_operands(torch, (m, nn, k), dev, args.dtype)
-                    c = torch.empty((m, nn), dtype=torch.float32, device=dev)
-                us = time_calls_alone(torch, gemm, a, b, c, CALLS[n])
-                results[n].append(us)
-                log(f"[bench] sweep {sweep} {n}: median {us:.2f} us/call")
-                del a, b, c
-                torch.cuda.empty_cache()
-        for n in names:
-            m, nn, k = table[n]
-            f, by = algorithmic(m, nn, k)
-            lo, hi = min(results[n]), max(results[n])
-            mid = (lo + hi) / 2
-            t_roof = max(f / (PEAK_TFLOPS * 1e12), by / (HBM_PEAK_GBS * 1e9))
-            entry = {"workload": n, "M": m, "N": nn, "K": k, "us_per_call": [round(lo, 3),
-                     round(hi, 3)], "tflops": round(f / (mid * 1e-6) / 1e12, 2),
-                     "bound": "mfma" if f / by > PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-                     else "hbm",
-                     "roofline_frac": round(t_roof / (mid * 1e-6), 4),
-                     "mfma_peak_frac": round(f / (mid * 1e-6) / 1e12 / PEAK_TFLOPS, 4),
-                     "calls": CALLS[n], "plan": gemm.gemm_f16_f32_abt_describe(m, nn, k)}
-            if n in PAGE_US:
-                entry["pages_b200_us"] = PAGE_US[n]
-            shapes.append(entry)
-
-    long_k = []
-    pages_inputs = None
-    if name == "8192^3" and not args.no_extras:
-        # The two long-K workloads, back to back like the headline, so every
-        # bench line carries their fraction of peak as well (not the value).
-        for n in ("2048x2048x16384", "1024x1024x65536"):
-            m, nn, k = inputs.WORKLOADS[n]
-            _, _, a, b = make_device_operands(torch, (m, nn, k), dev, args.dtype)
-            c = torch.empty((m, nn), dtype=torch.float32, device=dev)
-            # the board's clocks settle over the first ~100 calls of a new shape
-            avg_us = time_loop(torch, gemm, a, b, c, 200, 100)
-            f, _ = algorithmic(m, nn, k)
-            long_k.append({"workload": n, "us_per_call": round(avg_us, 3),
-                           "tflops": round(f / (avg_us * 1e-6) / 1e12, 2),
-                           "mfma_peak_frac": round(f / (avg_us * 1e-6) / 1e12 / PEAK_TFLOPS, 4),
-                           "calls": 200, "plan": gemm.gemm_f16_f32_abt_describe(m, nn, k)})
-            log(f"[bench] {n}: {avg_us:.2f} us/call back to back "
-                f"({long_k[-1]['mfma_peak_frac'] * 100:.1f}% of peak)")
-            del a, b, c
-            torch.cuda.empty_cache()
+        cache = {}
+        if name in table and args.inputs == "uniform":
+            cache[name] = (At, Bt, C)
+        t0 = time.perf_counter()
+        configs = measure_configs(torch, gemm, table, dev, args.dtype, args.sweeps, spinner, cache,
+                                  probe)
+        t1 = time.perf_counter()
+        del cache
+        torch.cuda.empty_cache()
+        log(f"[bench] configs measured in {t1 - t0:.1f} s (spin ahead of each call alone: "
+            f"{spinner.us} us)")
         # The same workload on the input kind the pages time on (integers in
         # [-3, 3] from a hash of the index): context for the data-dependent
         # power draw, never the value.
-        if args.dtype == "f16":
+        if args.dtype == "f16" and args.inputs == "uniform":
             a = torch.from_numpy(inputs.hash_int(M, K, 1)).to(dev)
             b = torch.from_numpy(inputs.hash_int(N, K, 2)).to(dev)
-            avg_us = time_loop(torch, gemm, a, b, C, args.steps, args.warmup)
+            el, kus, sclk_h = time_headline(torch, gemm, a, b, C, args.steps, args.warmup,
+                                            probe)
+            avg_us = float(np.mean(kus))
             pages_inputs = {"workload": name, "inputs": "hash_int [-3, 3]",
-                            "us_per_call": round(avg_us, 3),
+                            "kernel_us_mean": round(avg_us, 3),
+                            "kernel_us_median": round(float(np.median(kus)), 3),
                             "tflops": round(flops / (avg_us * 1e-6) / 1e12, 2),
-                            "mfma_peak_frac": round(flops / (avg_us * 1e-6) / 1e12 / PEAK_TFLOPS, 4),
-                            "calls": args.steps}
+                            "mfma_peak_frac": round(flops / (avg_us * 1e-6) / 1e12
+                                                    / PEAK_TFLOPS, 4),
+                            "calls": args.steps, "sclk_mhz": sclk_h}
+            if sclk_h:
+                pages_inputs["frac_at_sclk"] = round(pages_inputs["mfma_peak_frac"]
+                                                     * PEAK_SCLK_MHZ / sclk_h, 4)
             log(f"[bench] {name} on hash-integer inputs: {avg_us:.2f} us/call "
-                f"({pages_inputs['mfma_peak_frac'] * 100:.1f}% of peak)")
+                f"({pages_inputs['mfma_peak_frac'] * 100:.1f}% of peak) at {sclk_h} MHz")
             del a, b
             torch.cuda.empty_cache()
+    sus = None
+    if not args.no_telemetry:
+        sampler = ClockSampler()
+        sus = sustained(torch, gemm, At, Bt, C, flops, probe, sampler)
+        log(f"[bench] sustained: {sus}")
 
     vendor = None
     if args.vendor:
-        vendor = vendor_arm(torch, gemm, list(inputs.WORKLOADS), dev)
-
-    tele = None if args.no_telemetry else telemetry(torch, gemm, At, Bt, C)
-    if tele is not None:
-        log(f"[bench] telemetry: gfx clocks {tele['gfx_clk_mhz']} MHz, "
-            f"socket power {tele['socket_power_w']} W")
+        vendor = vendor_arm(torch, gemm, list(inputs.WORKLOADS), dev, Spinner(torch))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -518,19 +729,25 @@ def main():
         log(f"[bench] cpu: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
 
     vs = None
-    if name in PAGE_US and args.dtype == "f16":  # the pages time binary16 only
-        vs = round(value / (flops / (PAGE_US[name] * 1e-6) / 1e12), 4)
+    if name in PAGE_US and args.dtype == "f16" and args.inputs == "uniform":
+        vs = round(value / (flops / (PAGE_US[name] * 1e-6) / 1e12), 4)  # pages: binary16
+    data = {"uniform": f"synthetic: uniform[-1,1] {args.dtype}, seeds 1 (A) and 2 (B), "
+                       "resident in HBM",
+            "hash_int": "synthetic: integers in [-3,3] from a hash of the index (the pages' "
+                        "input kind), resident in HBM",
+            "integer": f"synthetic: integers in {{-2..2}} {args.dtype}, seeds 3 (A) and 4 (B), "
+                       "resident in HBM"}[args.inputs]
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": vs, "dtype": args.dtype,
-        "data": f"synthetic: uniform[-1,1] {args.dtype}, seeds 1 (A) and 2 (B), resident in HBM",
+        "data": data,
         "config": {"workload": f"gemm_abt {M}x{N}x{K}", "M": M, "N": N, "K": K,
                    "accumulate": "f32", "output": "f32",
                    "plan": gemm.gemm_f16_f32_abt_describe(M, N, K),
                    "source_hash": source_hash(), "library_md5": library_md5()},
-        "roofline": roofline, "cpu_baseline": cpu, "shapes": shapes, "long_k": long_k,
-        "pages_inputs": pages_inputs, "telemetry": tele,
+        "roofline": roofline, "cpu_baseline": cpu, "configs": configs,
+        "pages_inputs": pages_inputs, "sustained": sus,
     }
     if vendor is not None:
         line["vendor_hipblaslt"] = vendor

@@ -5,11 +5,13 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <unordered_map>
 #include <utility>
 
 #include "gemm_kernels.h"
@@ -93,22 +95,24 @@ gemm_status_t validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t l
   return GEMM_OK;
 }
 
-// Optional plan override for experiments and tests:
-// GEMM_F16_PLAN="kid=0,mode=1,splits=16,grid=256,group=4,xcd=0" (any subset of
-// keys), or "general=1" for the general kernel. Read on every plan; unknown
-// keys are ignored.
+// Plan override for experiments and tests, from text such as
+// "kid=35,mode=1,splits=16,grid=256,group=4,xcd=0,cus=32" (any subset of
+// keys), or "general=1" for the general kernel; unknown keys are ignored.
+// `cus` plans for that many compute units instead of the device's (the grid
+// never exceeds it). Set at first use from the environment variable
+// GEMM_F16_PLAN, and afterwards only by gemm_f16_set_plan_override.
 struct Override {
   int32_t kid = -1, mode = -1, splits = -1, grid = -1, group = -1, xcd = -1;
   int32_t general = 0;  // 1: the general kernel, whatever the operands
+  int32_t cus = -1;
 };
 
-Override read_override() {
+Override parse_override(const char* text) {
   Override o;
-  const char* env = std::getenv("GEMM_F16_PLAN");
-  if (!env) return o;
+  if (!text) return o;
   char buf[256];
-  std::snprintf(buf, sizeof(buf), "%s", env);
-  char* save = nullptr;  // strtok_r: calls may plan on several host threads at once
+  std::snprintf(buf, sizeof(buf), "%s", text);
+  char* save = nullptr;
   for (char* tok = strtok_r(buf, ",", &save); tok; tok = strtok_r(nullptr, ",", &save)) {
     char key[32];
     int val = 0;
@@ -120,6 +124,7 @@ Override read_override() {
     else if (!std::strcmp(key, "group")) o.group = val;
     else if (!std::strcmp(key, "xcd")) o.xcd = val;
     else if (!std::strcmp(key, "general")) o.general = val;
+    else if (!std::strcmp(key, "cus")) o.cus = val;
   }
   return o;
 }
@@ -158,8 +163,8 @@ bool tiled_eligible(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
 //     k-iterations is large enough: whole rounds data-parallel, the tiles
 //     left by stream-K (DP_SK).
 Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-               int64_t ldb, const float* C, int64_t ldc, int32_t cus, int32_t dt = DT_F16,
-               bool allow_pack = true);
+               int64_t ldb, const float* C, int64_t ldc, int32_t cus, int32_t dt,
+               const Override& o, bool allow_pack = true);
 
 // DP_SK: tiles below shared_base form whole data-parallel rounds of s.grid
 // tiles; the rest are shared by stream-K. Without a whole round it is plain
@@ -187,7 +192,8 @@ void set_shared_base(Sched& s) {
 // rounded up to 8 elements, zero-filled past K, at the end of the workspace,
 // and the tiled plan runs on the copies. Otherwise the general kernel.
 Plan packed_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-                 int64_t ldb, const float* C, int64_t ldc, int32_t cus, int32_t dt, int32_t kid) {
+                 int64_t ldb, const float* C, int64_t ldc, int32_t cus, int32_t dt, int32_t kid,
+                 const Override& o) {
   Plan general;
   general.kid = KID_GENERAL;
   if (K <= 0 || (double)M * (double)N * (double)K < kPackMinWork) return general;
@@ -197,7 +203,7 @@ Plan packed_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
   const bool pb = !operand_loadable(B, ldb, K, ki->bn, ki->bk);
   const void* aligned = (const void*)(uintptr_t)256;
   Plan p = make_plan(M, N, kp, pa ? aligned : A, pa ? kp : lda, pb ? aligned : B,
-                     pb ? kp : ldb, C, ldc, cus, dt, false);
+                     pb ? kp : ldb, C, ldc, cus, dt, o, false);
   if (p.kid < 0 || p.kid == KID_GENERAL) return general;
   p.pack_a = pa;
   p.pack_b = pb;
@@ -210,11 +216,10 @@ Plan packed_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
 
 Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                int64_t ldb, const float* C, int64_t ldc, int32_t cus, int32_t dt,
-               bool allow_pack) {
+               const Override& o, bool allow_pack) {
   Plan plan;
   if (M == 0 || N == 0) return plan;
   plan.c_vec4 = ((uintptr_t)C % 16 == 0) && (ldc % 4 == 0);
-  const Override o = read_override();
   if (o.general == 1) {
     plan.kid = KID_GENERAL;
     return plan;
@@ -244,7 +249,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
   if (o.splits >= 1) splits = o.splits;
 
   if (!tiled_eligible(M, N, K, A, lda, B, ldb, kid)) {
-    if (allow_pack) return packed_plan(M, N, K, A, lda, B, ldb, C, ldc, cus, dt, kid);
+    if (allow_pack) return packed_plan(M, N, K, A, lda, B, ldb, C, ldc, cus, dt, kid, o);
     plan.kid = KID_GENERAL;
     return plan;
   }
@@ -315,19 +320,102 @@ const char* mode_name(int32_t m) {
   }
 }
 
-// Device CU counts, cached per device.
-std::mutex g_cus_mu;
-std::map<int, int32_t> g_cus;
+// Device CU counts, cached per device (0: not asked yet).
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t> g_cus[kMaxDevices];
 
 int32_t device_cus(int dev) {
-  std::lock_guard<std::mutex> lock(g_cus_mu);
-  auto it = g_cus.find(dev);
-  if (it != g_cus.end()) return it->second;
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    n = kDefaultCUs;
-  g_cus[dev] = n;
-  return n;
+  if (dev < 0 || dev >= kMaxDevices) return kDefaultCUs;
+  int32_t n = g_cus[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  int q = 0;
+  if (hipDeviceGetAttribute(&q, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || q <= 0)
+    q = kDefaultCUs;
+  g_cus[dev].store(q, std::memory_order_relaxed);
+  return q;
+}
+
+// Plans are cached per call signature: the shape, the row strides, whether
+// each of A, B and C is 16-byte aligned (all make_plan looks at in the
+// pointers), the operand type and the CU count. The override is part of the
+// state the cache holds; changing it empties the cache.
+struct PlanKey {
+  int64_t M, N, K, lda, ldb, ldc;
+  int32_t aligned;  // bit 0: A, bit 1: B, bit 2: C 16-byte aligned
+  int32_t dt, cus;
+  bool operator==(const PlanKey& o) const {
+    return M == o.M && N == o.N && K == o.K && lda == o.lda && ldb == o.ldb && ldc == o.ldc &&
+           aligned == o.aligned && dt == o.dt && cus == o.cus;
+  }
+};
+
+struct PlanKeyHash {
+  size_t operator()(const PlanKey& k) const {
+    uint64_t h = 0x9E3779B97F4A7C15ull;
+    const int64_t v[9] = {k.M, k.N, k.K, k.lda, k.ldb, k.ldc, k.aligned, k.dt, k.cus};
+    for (int64_t x : v) {
+      h ^= (uint64_t)x + 0x9E3779B97F4A7C15ull + (h << 6) + (h >> 2);
+    }
+    return (size_t)h;
+  }
+};
+
+constexpr size_t kPlanCacheMax = 4096;  // emptied when it grows past this
+std::mutex g_plan_mu;
+bool g_override_set = false;
+Override g_override;
+std::unordered_map<PlanKey, Plan, PlanKeyHash> g_plans;
+
+// The caller holds g_plan_mu.
+const Override& current_override() {
+  if (!g_override_set) {
+    g_override = parse_override(std::getenv("GEMM_F16_PLAN"));
+    g_override_set = true;
+  }
+  return g_override;
+}
+
+// CU count plans are made for: the override's, else the device's (dev >= 0),
+// else a whole MI355X. The caller holds g_plan_mu.
+int32_t planning_cus(int dev) {
+  const Override& o = current_override();
+  if (o.cus > 0) return o.cus;
+  return dev >= 0 ? device_cus(dev) : kDefaultCUs;
+}
+
+// The plan for a call (cached). dev: the current device, or -1 for none.
+Plan lookup_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                 int64_t ldb, const float* C, int64_t ldc, int32_t dt, int dev) {
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  const int32_t cus = planning_cus(dev);
+  const PlanKey key{M, N, K, lda, ldb, ldc,
+                    (((uintptr_t)A & 15) == 0 ? 1 : 0) | (((uintptr_t)B & 15) == 0 ? 2 : 0) |
+                        (((uintptr_t)C & 15) == 0 ? 4 : 0),
+                    dt, cus};
+  auto it = g_plans.find(key);
+  if (it != g_plans.end()) return it->second;
+  const Plan plan = make_plan(M, N, K, A, lda, B, ldb, C, ldc, cus, dt, current_override());
+  if (g_plans.size() >= kPlanCacheMax) g_plans.clear();
+  g_plans.emplace(key, plan);
+  return plan;
+}
+
+// The plan the entry points take for aligned operands with row strides of K
+// (rounded up to 8) and ldc = N: what describe, workspace_size and the
+// schedule model report. dev as in lookup_plan.
+Plan reference_plan(int64_t M, int64_t N, int64_t K, int dev) {
+  const void* aligned = (const void*)(uintptr_t)256;
+  const int64_t ld = K % 8 ? K + (8 - K % 8) : K;
+  return lookup_plan(M, N, K, aligned, ld, aligned, ld, (const float*)aligned, N, DT_F16, dev);
+}
+
+// Clock probe counters for every later launch (nullptr: off).
+std::atomic<unsigned long long*> g_clock_probe{nullptr};
+
+// The current device, or -1 when none is usable.
+int current_device() {
+  int dev = 0;
+  return hipGetDevice(&dev) == hipSuccess ? dev : -1;
 }
 
 // Library-owned workspaces (partial tiles of split-K / stream-K plans), one
@@ -392,16 +480,25 @@ gemm_status_t run(int32_t dt, int64_t M, int64_t N, int64_t K, const void* A, in
   if (st != GEMM_OK) return st;
   if (M == 0 || N == 0) return GEMM_OK;
   hipStream_t stream = (hipStream_t)stream_v;
-  int dev = 0;
+  // One plan per call, for the CU count gemm_f16_f32_abt_workspace_size also
+  // uses; the caller's workspace is checked against it before anything is
+  // enqueued.
+  const int dev = current_device();
+  Plan plan = lookup_plan(M, N, K, A, lda, B, ldb, C, ldc, dt, dev);
   if (caller_ws) {
-    // Checks on the caller's workspace come before any HIP call.
-    const Plan probe =
-        caller_plan(make_plan(M, N, K, A, lda, B, ldb, C, ldc, kDefaultCUs, dt), ws, ws_bytes);
-    if (!workspace_fits(probe, ws, ws_bytes)) return GEMM_ERR_WORKSPACE;
+    plan = caller_plan(plan, ws, ws_bytes);
+    if (!workspace_fits(plan, ws, ws_bytes)) return GEMM_ERR_WORKSPACE;
   }
-  if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
-  Plan plan = make_plan(M, N, K, A, lda, B, ldb, C, ldc, device_cus(dev), dt);
-  if (caller_ws) plan = caller_plan(plan, ws, ws_bytes);
+  if (dev < 0) return GEMM_ERR_HIP;
+  if (plan.kid != KID_GENERAL && !tiled_has(plan.kid, dt)) return GEMM_ERR_NOT_SUPPORTED;
+  if (plan.workspace > 0 && !caller_ws) {
+    // A library-owned workspace can be freed and replaced by a later call on
+    // this stream; a captured graph would keep its old address. Calls being
+    // captured therefore need a caller workspace.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return GEMM_ERR_HIP;
+    if (cap != hipStreamCaptureStatusNone) return GEMM_ERR_WORKSPACE;
+  }
   GemmParams p{};
   p.A = (const uint16_t*)A;
   p.B = (const uint16_t*)B;
@@ -414,15 +511,14 @@ gemm_status_t run(int32_t dt, int64_t M, int64_t N, int64_t K, const void* A, in
   p.K = (int32_t)K;
   p.c_vec4 = plan.c_vec4 ? 1 : 0;
   p.s = plan.s;
+  p.clock_probe = g_clock_probe.load(std::memory_order_relaxed);
   if (plan.kid == KID_GENERAL) {
     return launch_general(dt, p, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
   }
-  if (!tiled_has(plan.kid, dt)) return GEMM_ERR_NOT_SUPPORTED;
   std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);
   if (plan.workspace > 0) {
     void* w = nullptr;
     if (caller_ws) {
-      if (!workspace_fits(plan, ws, ws_bytes)) return GEMM_ERR_WORKSPACE;
       w = ws;
     } else {
       ws_lock.lock();  // released once the kernels are enqueued
@@ -472,19 +568,15 @@ gemm_status_t gemm_bf16_f32_abt(int64_t M, int64_t N, int64_t K, const void* A, 
 
 size_t gemm_f16_f32_abt_workspace_size(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K < 0) return 0;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
   // Aligned operands with K as the row stride: the plan the fast path takes,
-  // for the current device's CU count (a partitioned device has fewer CUs and
-  // may plan differently).
-  int dev = 0;
-  const int32_t cus = hipGetDevice(&dev) == hipSuccess ? device_cus(dev) : kDefaultCUs;
-  const void* aligned = (const void*)(uintptr_t)256;
-  const int64_t ld = K % 8 ? K + (8 - K % 8) : K;
-  const Plan plan = make_plan(M, N, K, aligned, ld, aligned, ld, (const float*)aligned, N, cus);
-  // With K not a multiple of 8 the rows of both operands are packed (no row
-  // stride makes them 16-byte aligned), and this includes the copies. Other
-  // misaligned operands pack only into a caller workspace large enough for
-  // them; otherwise that call runs the general kernel.
-  return plan.workspace;
+  // for the CU count the calls plan with (a partitioned device has fewer CUs
+  // and may plan differently). With K not a multiple of 8 the rows of both
+  // operands are packed (no row stride makes them 16-byte aligned), and this
+  // includes the copies. Other misaligned operands pack only into a caller
+  // workspace large enough for them; otherwise that call runs the general
+  // kernel.
+  return reference_plan(M, N, K, current_device()).workspace;
 }
 
 gemm_status_t gemm_f16_f32_abt_ws(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
@@ -520,10 +612,7 @@ gemm_status_t gemm_f16_f32_abt_describe(int64_t M, int64_t N, int64_t K, char* b
   if (buf == nullptr || len == 0) return GEMM_ERR_INVALID_VALUE;
   if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_VALUE;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_ERR_NOT_SUPPORTED;
-  const void* aligned = (const void*)(uintptr_t)256;
-  const int64_t ld = K % 8 ? K + (8 - K % 8) : K;
-  const Plan plan = make_plan(M, N, K, aligned, ld, aligned, ld, (const float*)aligned, N,
-                              kDefaultCUs);
+  const Plan plan = reference_plan(M, N, K, -1);
   if (plan.kid < 0) {
     std::snprintf(buf, len, "M=%lld N=%lld K=%lld: nothing to do", (long long)M, (long long)N,
                   (long long)K);
@@ -576,9 +665,7 @@ int64_t gemm_f16_schedule_dump(int64_t M, int64_t N, int64_t K, int64_t grid, in
                                int64_t cap, int64_t* k_iters, int64_t* tiles) {
   if (M <= 0 || N <= 0 || K <= 0 || cap < 0 || (cap > 0 && out == nullptr)) return -1;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return -1;
-  const void* aligned = (const void*)(uintptr_t)256;
-  const int64_t ld = K % 8 ? K + (8 - K % 8) : K;
-  Plan plan = make_plan(M, N, K, aligned, ld, aligned, ld, (const float*)aligned, N, kDefaultCUs);
+  Plan plan = reference_plan(M, N, K, -1);
   if (plan.kid < 0 || plan.kid == KID_GENERAL) return -1;
   Sched s = plan.s;
   if (grid > 0) {
@@ -611,5 +698,16 @@ int64_t gemm_f16_schedule_dump(int64_t M, int64_t N, int64_t K, int64_t grid, in
   return rows;
 }
 
+
+void gemm_f16_set_clock_probe(unsigned long long* counters) {
+  g_clock_probe.store(counters, std::memory_order_relaxed);
+}
+
+void gemm_f16_set_plan_override(const char* text) {
+  std::lock_guard<std::mutex> lock(g_plan_mu);
+  g_override = parse_override(text);
+  g_override_set = true;
+  g_plans.clear();
+}
 
 }  // extern "C"

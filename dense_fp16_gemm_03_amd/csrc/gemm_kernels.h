@@ -18,47 +18,20 @@ namespace g16 {
 // replaces; PP 1 selects the ping-pong main loop (two wave groups, one
 // computing while the other reads LDS and issues loads), PP 2 its form with
 // two stages 64 wide in k (whole 128-byte rows per load).
-#define G16_TILED_KERNELS(X)                                       \
-  X(0, KID_256x256x64_S2_W4, 256, 256, 64, 2, 2, 2, 32, 0, 0)            \
-  X(1, KID_256x256x32_S4_W4, 256, 256, 32, 4, 2, 2, 32, 0, 0)            \
-  X(2, KID_256x256x64_S2_W8, 256, 256, 64, 2, 2, 4, 32, 0, 0)            \
-  X(3, KID_256x128x64_S3_W4, 256, 128, 64, 3, 2, 2, 32, 0, 0)            \
-  X(4, KID_128x128x64_S4_W4, 128, 128, 64, 4, 2, 2, 32, 0, 0)            \
-  X(5, KID_128x64x64_S4_W4, 128, 64, 64, 4, 2, 2, 32, 0, 0)              \
-  X(6, KID_64x64x64_S4_W4, 64, 64, 64, 4, 2, 2, 32, 0, 0)                \
-  X(7, KID_256x256x32_S5_W4, 256, 256, 32, 5, 2, 2, 32, 0, 0)            \
-  X(8, KID_256x256x32_S4_W8, 256, 256, 32, 4, 2, 4, 32, 0, 0)            \
-  X(9, KID_256x256x32_S5_W8, 256, 256, 32, 5, 2, 4, 32, 0, 0)            \
-  X(10, KID_256x256x64_S2_W4_M16, 256, 256, 64, 2, 2, 2, 16, 0, 0)       \
-  X(11, KID_256x256x32_S4_W4_M16, 256, 256, 32, 4, 2, 2, 16, 0, 0)       \
-  X(12, KID_256x256x32_S5_W4_M16, 256, 256, 32, 5, 2, 2, 16, 0, 0)       \
-  X(13, KID_256x256x64_S2_W8_M16, 256, 256, 64, 2, 2, 4, 16, 0, 0)       \
-  X(14, KID_256x256x32_S5_W8_M16, 256, 256, 32, 5, 2, 4, 16, 0, 0)       \
-  X(15, KID_256x128x64_S3_W4_M16, 256, 128, 64, 3, 2, 2, 16, 0, 0)       \
-  X(16, KID_128x128x64_S4_W4_M16, 128, 128, 64, 4, 2, 2, 16, 0, 0)       \
-  X(17, KID_128x64x64_S4_W4_M16, 128, 64, 64, 4, 2, 2, 16, 0, 0)         \
-  X(18, KID_64x64x64_S4_W4_M16, 64, 64, 64, 4, 2, 2, 16, 0, 0)           \
-  X(19, KID_256x256x32_S3_W4_M16, 256, 256, 32, 3, 2, 2, 16, 0, 0)   \
-  X(20, KID_256x256x32_S5_W8_M16_RS, 256, 256, 32, 5, 2, 4, 16, 1, 0) \
-  X(21, KID_256x256x64_S2_W8_M16_RS, 256, 256, 64, 2, 2, 4, 16, 1, 0) \
-  X(22, KID_256x256x32_S4_W8_M16_RS, 256, 256, 32, 4, 2, 4, 16, 1, 0) \
-  X(23, KID_256x256x32_S5_W4_M16_RS, 256, 256, 32, 5, 2, 2, 16, 1, 0) \
-  X(24, KID_256x256x64_S2_W4_M16_RS, 256, 256, 64, 2, 2, 2, 16, 1, 0) \
-  X(25, KID_256x256x32_S5_W8_M16_PP, 256, 256, 32, 5, 2, 4, 16, 0, 1) \
-  X(26, KID_256x256x32_S4_W8_M16_PP, 256, 256, 32, 4, 2, 4, 16, 0, 1) \
-  X(27, KID_256x256x32_S3_W8_M16_PP, 256, 256, 32, 3, 2, 4, 16, 0, 1) \
-  X(28, KID_256x256x32_S5_W8_PP, 256, 256, 32, 5, 2, 4, 32, 0, 1)     \
-  X(29, KID_256x128x32_S5_W8_M16_PP, 256, 128, 32, 5, 2, 4, 16, 0, 1) \
-  X(30, KID_64x64x64_S8_W4_M16, 64, 64, 64, 8, 2, 2, 16, 0, 0)         \
-  X(31, KID_64x64x32_S10_W4_M16, 64, 64, 32, 10, 2, 2, 16, 0, 0)       \
-  X(32, KID_128x64x64_S6_W4_M16, 128, 64, 64, 6, 2, 2, 16, 0, 0)       \
-  X(33, KID_64x64x64_S8_W4, 64, 64, 64, 8, 2, 2, 32, 0, 0)             \
-  X(34, KID_128x128x64_S4_W4_M16_RS, 128, 128, 64, 4, 2, 2, 16, 1, 0) \
-  X(35, KID_256x256x64_S2_W8_M16_PP, 256, 256, 64, 2, 2, 4, 16, 0, 2)
+// Only the kernels the shape rule picks are built (16, 18, 27, 35), plus the
+// v_mfma_f32_32x32x16_f16 forms of the two ping-pong loops (28, 36), which
+// the plan override can select to compare the two MFMA shapes on the same
+// main loop. Ids are stable: a removed variant's id is never reused.
+#define G16_TILED_KERNELS(X)                                           \
+  X(16, KID_128x128x64_S4_W4_M16, 128, 128, 64, 4, 2, 2, 16, 0, 0)     \
+  X(18, KID_64x64x64_S4_W4_M16, 64, 64, 64, 4, 2, 2, 16, 0, 0)         \
+  X(27, KID_256x256x32_S3_W8_M16_PP, 256, 256, 32, 3, 2, 4, 16, 0, 1)  \
+  X(28, KID_256x256x32_S5_W8_PP, 256, 256, 32, 5, 2, 4, 32, 0, 1)      \
+  X(35, KID_256x256x64_S2_W8_M16_PP, 256, 256, 64, 2, 2, 4, 16, 0, 2)  \
+  X(36, KID_256x256x64_S2_W8_PP, 256, 256, 64, 2, 2, 4, 32, 0, 2)
 
-// Kernel ids also built for bfloat16 operands (the shape rule's picks, and
-// the other ping-pong depths).
-#define G16_BF16_KERNELS(X) X(16) X(18) X(25) X(26) X(27) X(35)
+// Kernel ids also built for bfloat16 operands (the shape rule's picks).
+#define G16_BF16_KERNELS(X) X(16) X(18) X(27) X(35)
 
 // Operand element types.
 enum DType : int32_t { DT_F16 = 0, DT_BF16 = 1 };
@@ -66,7 +39,7 @@ enum DType : int32_t { DT_F16 = 0, DT_BF16 = 1 };
 #define G16_KID_ENUM(id, name, ...) name = id,
 enum KernelId : int32_t {
   G16_TILED_KERNELS(G16_KID_ENUM)
-  KID_COUNT = 36,
+  KID_COUNT = 37,  // one past the largest id (ids in between may be unused)
   KID_GENERAL = 100  // any shape and alignment, 64 x 64 tiles, no LDS
 };
 #undef G16_KID_ENUM
@@ -92,6 +65,10 @@ struct GemmParams {
   int32_t M, N, K;
   int32_t c_vec4;  // C base and ldc allow 16-byte stores
   Sched s;
+  // Clock probe (nullptr: off). Workgroup 0 of the main kernel adds the
+  // shader-clock cycles and the 100 MHz real-time ticks between its start and
+  // its end to clock_probe[0] and clock_probe[1].
+  unsigned long long* clock_probe;
 };
 
 // Launches the tiled kernel `kid` for operand type `dt` with p.s.grid

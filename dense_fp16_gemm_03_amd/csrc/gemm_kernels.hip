@@ -230,6 +230,38 @@ __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Clock probe: wave 0 of workgroup 0 reads the shader-clock counter
+// (s_memtime) and the constant 100 MHz real-time counter (s_memrealtime) when
+// it starts and when it ends, and lane 0 adds both differences to the
+// caller's counters, so their ratio over any number of launches is the
+// average shader clock while those launches ran. Off (one uniform branch)
+// when the pointer is null.
+struct ClockProbe {
+  unsigned long long cycles = 0, ticks = 0;
+  bool on = false;
+};
+
+__device__ __forceinline__ ClockProbe probe_start(const GemmParams& p, int wave) {
+  ClockProbe c;
+  c.on = p.clock_probe != nullptr && blockIdx.x == 0 && wave == 0;
+  if (c.on) {
+    c.cycles = __builtin_amdgcn_s_memtime();
+    c.ticks = __builtin_amdgcn_s_memrealtime();
+  }
+  return c;
+}
+
+__device__ __forceinline__ void probe_end(const GemmParams& p, const ClockProbe& c, int lane) {
+  if (c.on) {
+    const unsigned long long cycles = __builtin_amdgcn_s_memtime() - c.cycles;
+    const unsigned long long ticks = __builtin_amdgcn_s_memrealtime() - c.ticks;
+    if (lane == 0) {
+      atomicAdd(p.clock_probe, cycles);
+      atomicAdd(p.clock_probe + 1, ticks);
+    }
+  }
+}
+
 template <class C>
 struct Frags {
   typename C::M::frag_t a[C::FM];
@@ -663,6 +695,7 @@ void gemm_tiled_kernel(GemmParams p) {
   const int wm = wave / C::WGN;
   const int wn = wave % C::WGN;
   const int v = virtual_wg(blockIdx.x, p.s.grid, p.s.xcd_remap);
+  const ClockProbe probe = probe_start(p, wave);
 
   Segment seg;
   for (int n = 0; seg_at_uniform(p.s, v, n, &seg); ++n) {
@@ -734,6 +767,7 @@ void gemm_tiled_kernel(GemmParams p) {
                        acc, wave, lane);
     }
   }
+  probe_end(p, probe, lane);
 }
 
 // Per-unit state of the load stream: operand windows, per-lane load map and
@@ -811,6 +845,7 @@ void gemm_pingpong_kernel(GemmParams p) {
   const int wm = wave / C::WGN;
   const int wn = wave % C::WGN;
   const int v = virtual_wg(blockIdx.x, p.s.grid, p.s.xcd_remap);
+  const ClockProbe probe = probe_start(p, wave);
 
   Segment seg;
   if (!seg_at_uniform(p.s, v, 0, &seg)) return;
@@ -908,6 +943,7 @@ void gemm_pingpong_kernel(GemmParams p) {
     if (!late) phase_barrier();
     if (!more) break;
   }
+  probe_end(p, probe, lane);
 }
 
 // Ping-pong main loop over stages 64 wide in k, two of them in LDS (128 KiB),
@@ -930,7 +966,10 @@ __global__ __launch_bounds__(C::THREADS)
 __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_EU, C::WAVES_PER_EU)))
 void gemm_pingpong64_kernel(GemmParams p) {
   static_assert(C::WAVES == 8, "ping-pong pairs two waves per SIMD");
-  static_assert(C::STAGES == 2 && C::KSTEPS == 2, "two stages of two k-steps");
+  static_assert(C::STAGES == 2 && C::BK == 64, "two stages 64 wide in k");
+  // MFMA k-steps per phase: a phase covers 32 of k (one 16x16x32 k-step, or
+  // two 32x32x16 ones).
+  constexpr int KPP = C::KSTEPS / 2;
   constexpr int kStores = epilogue_stores<C>();
   static_assert(C::LOADS + kStores <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
@@ -942,6 +981,7 @@ void gemm_pingpong64_kernel(GemmParams p) {
   const int wm = wave / C::WGN;
   const int wn = wave % C::WGN;
   const int v = virtual_wg(blockIdx.x, p.s.grid, p.s.xcd_remap);
+  const ClockProbe probe = probe_start(p, wave);
 
   Segment seg;
   if (!seg_at_uniform(p.s, v, 0, &seg)) return;
@@ -966,13 +1006,14 @@ void gemm_pingpong64_kernel(GemmParams p) {
     phase_barrier();
     if (late) phase_barrier();  // group 1 starts one phase behind
 
-    Frags<C> fr;
+    Frags<C> fr[KPP];
     for (int it = 0; it < u.nk; ++it) {
       const char* stage = smem + (it & 1) * C::STAGE_BYTES;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         // Memory phase.
-        read_frags<C>(stage, ks, wm, wn, lane, fr);
+#pragma unroll
+        for (int kk = 0; kk < KPP; ++kk) read_frags<C>(stage, ks * KPP + kk, wm, wn, lane, fr[kk]);
         if (ks == 0) {
           if (it + 1 < u.nk) {
             const int k0 = (u.k_begin + it + 1) * C::BK;
@@ -987,12 +1028,14 @@ void gemm_pingpong64_kernel(GemmParams p) {
         phase_barrier();
         // Compute phase (serpentine order, as in gemm_pingpong_kernel).
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
+        for (int kk = 0; kk < KPP; ++kk)
 #pragma unroll
-          for (int jj = 0; jj < C::FN; ++jj) {
-            const int j = (i & 1) ? C::FN - 1 - jj : jj;
-            acc[i][j] = C::M::mma(fr.b[j], fr.a[i], acc[i][j]);
-          }
+          for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < C::FN; ++jj) {
+              const int j = (i & 1) ? C::FN - 1 - jj : jj;
+              acc[i][j] = C::M::mma(fr[kk].b[j], fr[kk].a[i], acc[i][j]);
+            }
         phase_barrier();
       }
     }
@@ -1023,6 +1066,7 @@ void gemm_pingpong64_kernel(GemmParams p) {
     if (!late) phase_barrier();
     if (!more) break;
   }
+  probe_end(p, probe, lane);
 }
 
 // Shares of output tile t under schedule s (1: the tile was stored directly).
@@ -1155,29 +1199,14 @@ constexpr KernelInfo info_of(const char* name) {
   return KernelInfo{C::BM, C::BN, C::BK, C::STAGES, C::WAVES, C::LDS_BYTES, C::MI, name};
 }
 
-// Names: BMxBNxBK, ring depth, waves, "_m16" for the 16x16x32 MFMA, "_rs"
-// for late fragment reads and "_pp" for the ping-pong main loop.
-constexpr KernelInfo kInfos[KID_COUNT] = {
-    info_of<K0>("256x256x64_s2_w4"),      info_of<K1>("256x256x32_s4_w4"),
-    info_of<K2>("256x256x64_s2_w8"),      info_of<K3>("256x128x64_s3_w4"),
-    info_of<K4>("128x128x64_s4_w4"),      info_of<K5>("128x64x64_s4_w4"),
-    info_of<K6>("64x64x64_s4_w4"),        info_of<K7>("256x256x32_s5_w4"),
-    info_of<K8>("256x256x32_s4_w8"),      info_of<K9>("256x256x32_s5_w8"),
-    info_of<K10>("256x256x64_s2_w4_m16"), info_of<K11>("256x256x32_s4_w4_m16"),
-    info_of<K12>("256x256x32_s5_w4_m16"), info_of<K13>("256x256x64_s2_w8_m16"),
-    info_of<K14>("256x256x32_s5_w8_m16"), info_of<K15>("256x128x64_s3_w4_m16"),
-    info_of<K16>("128x128x64_s4_w4_m16"), info_of<K17>("128x64x64_s4_w4_m16"),
-    info_of<K18>("64x64x64_s4_w4_m16"),   info_of<K19>("256x256x32_s3_w4_m16"),
-    info_of<K20>("256x256x32_s5_w8_m16_rs"), info_of<K21>("256x256x64_s2_w8_m16_rs"),
-    info_of<K22>("256x256x32_s4_w8_m16_rs"), info_of<K23>("256x256x32_s5_w4_m16_rs"),
-    info_of<K24>("256x256x64_s2_w4_m16_rs"),
-    info_of<K25>("256x256x32_s5_w8_m16_pp"), info_of<K26>("256x256x32_s4_w8_m16_pp"),
-    info_of<K27>("256x256x32_s3_w8_m16_pp"), info_of<K28>("256x256x32_s5_w8_pp"),
-    info_of<K29>("256x128x32_s5_w8_m16_pp"),
-    info_of<K30>("64x64x64_s8_w4_m16"),      info_of<K31>("64x64x32_s10_w4_m16"),
-    info_of<K32>("128x64x64_s6_w4_m16"),     info_of<K33>("64x64x64_s8_w4"),
-    info_of<K34>("128x128x64_s4_w4_m16_rs"), info_of<K35>("256x256x64_s2_w8_m16_pp"),
-};
+// Names: BMxBNxBK, ring depth, waves, "_m16" for the 16x16x32 MFMA and
+// "_pp" for the ping-pong main loop.
+constexpr KernelInfo kInfo16 = info_of<K16>("128x128x64_s4_w4_m16");
+constexpr KernelInfo kInfo18 = info_of<K18>("64x64x64_s4_w4_m16");
+constexpr KernelInfo kInfo27 = info_of<K27>("256x256x32_s3_w8_m16_pp");
+constexpr KernelInfo kInfo28 = info_of<K28>("256x256x32_s5_w8_pp");
+constexpr KernelInfo kInfo35 = info_of<K35>("256x256x64_s2_w8_m16_pp");
+constexpr KernelInfo kInfo36 = info_of<K36>("256x256x64_s2_w8_pp");
 
 template <class C>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t stream) {
@@ -1218,8 +1247,13 @@ int32_t occupancy_cfg() {
 }  // namespace
 
 const KernelInfo* kernel_info(int32_t kid) {
-  if (kid < 0 || kid >= KID_COUNT) return nullptr;
-  return &kInfos[kid];
+#define G16_INFO(id, name, ...) \
+  case name: return &kInfo##id;
+  switch (kid) {
+    G16_TILED_KERNELS(G16_INFO)
+    default: return nullptr;
+  }
+#undef G16_INFO
 }
 
 hipError_t launch_tiled(int32_t kid, int32_t dt, const GemmParams& p, hipStream_t stream) {
@@ -1242,7 +1276,7 @@ hipError_t launch_tiled(int32_t kid, int32_t dt, const GemmParams& p, hipStream_
 }
 
 bool tiled_has(int32_t kid, int32_t dt) {
-  if (kid < 0 || kid >= KID_COUNT) return false;
+  if (kernel_info(kid) == nullptr) return false;
   if (dt == DT_F16) return true;
   if (dt != DT_BF16) return false;
 #define G16_HAS_BF16(id) if (kid == id) return true;

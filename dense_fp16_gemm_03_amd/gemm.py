@@ -26,7 +26,7 @@ EXPORTS = (
     "gemm_status_string", "gemm_f16_f32_abt_describe", "gemm_f16_release_workspaces",
     "gemm_f16_schedule_dump", "gemm_f16_lds_chunk", "gemm_bf16_f32_abt",
     "gemm_bf16_f32_abt_workspace_size",
-    "gemm_bf16_f32_abt_ws",
+    "gemm_bf16_f32_abt_ws", "gemm_f16_set_plan_override", "gemm_f16_set_clock_probe",
 )
 
 _lib = None
@@ -71,6 +71,10 @@ def load(path: str = LIBRARY):
     lib.gemm_f16_schedule_dump.restype = i64
     lib.gemm_f16_lds_chunk.argtypes = [ctypes.c_int32] * 4
     lib.gemm_f16_lds_chunk.restype = ctypes.c_int32
+    lib.gemm_f16_set_plan_override.argtypes = [ctypes.c_char_p]
+    lib.gemm_f16_set_plan_override.restype = None
+    lib.gemm_f16_set_clock_probe.argtypes = [p]
+    lib.gemm_f16_set_clock_probe.restype = None
     if path == LIBRARY:
         _lib = lib
     return lib
@@ -128,6 +132,16 @@ def gemm_f16_release_workspaces() -> None:
     load().gemm_f16_release_workspaces()
 
 
+def gemm_f16_set_plan_override(text: str = "") -> None:
+    """Plan override for tests and experiments ("" restores the default rule)."""
+    load().gemm_f16_set_plan_override(text.encode() if text else None)
+
+
+def gemm_f16_set_clock_probe(counters: int = 0) -> None:
+    """Clock probe: device address of two uint64 counters (0 turns it off)."""
+    load().gemm_f16_set_clock_probe(counters or None)
+
+
 def gemm_f16_lds_chunk(chunks_per_row, block_dim, row, chunk) -> int:
     """LDS position of logical chunk `chunk` of tile row `row` (-1: bad arguments)."""
     return load().gemm_f16_lds_chunk(chunks_per_row, block_dim, row, chunk)
@@ -161,38 +175,52 @@ def gemm_abt(A, B, C=None, stream=None, workspace=None):
     its own per-stream workspace."""
     import torch
 
-    if A.dtype != B.dtype or A.dtype not in (torch.float16, torch.bfloat16):
+    global _DTYPES
+    if _DTYPES is None:
+        _DTYPES = (torch.float16, torch.bfloat16)
+    dt = A.dtype
+    if dt != B.dtype or dt not in _DTYPES:
         raise TypeError("A and B must be both float16 or both bfloat16")
-    bf16 = A.dtype == torch.bfloat16
     if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[1]:
         raise ValueError("A must be (M, K) and B (N, K)")
     M, K = A.shape
     N = B.shape[0]
+    dev = A.device
     if C is None:
-        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
-    if C.dtype != torch.float32 or tuple(C.shape) != (M, N):
+        C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    elif C.dtype != torch.float32 or C.shape != (M, N):
         raise ValueError("C must be float32 (M, N)")
     for t, name in ((A, "A"), (B, "B"), (C, "C")):
-        if not t.is_cuda or t.device != A.device:
+        if t.device != dev or not t.is_cuda:
             raise ValueError(f"{name} must be on A's GPU")
         if t.shape[1] > 1 and t.stride(1) != 1 and t.numel() > 0:
             raise ValueError(f"{name} must have unit stride along its last dimension")
-    if workspace is not None and (not workspace.is_cuda or workspace.device != A.device
+    if workspace is not None and (not workspace.is_cuda or workspace.device != dev
                                   or not workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous tensor on A's GPU")
     lda = A.stride(0) if M > 1 else max(K, 1)
     ldb = B.stride(0) if N > 1 else max(K, 1)
     ldc = C.stride(0) if M > 1 else max(N, 1)
     if stream is None:
-        stream = torch.cuda.current_stream(A.device)
+        stream = torch.cuda.current_stream(dev)
     s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    with torch.cuda.device(A.device):
-        if workspace is None:
-            fn = gemm_bf16_f32_abt if bf16 else gemm_f16_f32_abt
-            st = fn(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, s)
-        else:
-            fn = gemm_bf16_f32_abt_ws if bf16 else gemm_f16_f32_abt_ws
-            st = fn(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,
-                    workspace.data_ptr(), workspace.numel() * workspace.element_size(), s)
+    lib = _lib if _lib is not None else load()
+    bf16 = dt == torch.bfloat16
+    if workspace is None:
+        fn = lib.gemm_bf16_f32_abt if bf16 else lib.gemm_f16_f32_abt
+        args = (M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, s)
+    else:
+        fn = lib.gemm_bf16_f32_abt_ws if bf16 else lib.gemm_f16_f32_abt_ws
+        args = (M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,
+                workspace.data_ptr(), workspace.numel() * workspace.element_size(), s)
+    # the library works on the current HIP device: make it A's for the call
+    if dev.index == torch.cuda.current_device():
+        st = fn(*args)
+    else:
+        with torch.cuda.device(dev):
+            st = fn(*args)
     _check(st)
     return C
+
+
+_DTYPES = None  # (torch.float16, torch.bfloat16), set at the first call

@@ -19,8 +19,15 @@
  * stream) of the current HIP device and the call returns without waiting.
  * The caller owns A, B, C and any workspace and keeps them alive until the
  * stream work finishes. The library never frees or retains caller pointers.
- * Argument errors are reported before any HIP call; device faults surface at
- * the caller's next synchronisation. The library never aborts or prints.
+ * Argument errors (including a caller workspace that is too small) are
+ * reported before anything is enqueued; the call may query the current
+ * device first. Device faults surface at the caller's next synchronisation.
+ * The library never aborts or prints.
+ *
+ * Plans (kernel, tile, schedule) depend only on the shape, the row strides,
+ * whether each of A, B and C is 16-byte aligned, the operand type and the
+ * device's compute-unit count; they are made once per such signature and
+ * cached, so repeated calls pay only the argument checks and the launches.
  */
 #ifndef GEMM_F16_H
 #define GEMM_F16_H
@@ -59,7 +66,13 @@ typedef enum {
  * library-owned, allocated once per (device, stream) on first use and grown
  * when a larger one is needed; calls sharing a stream are ordered by it,
  * calls on different streams do not share one. Calls from several host
- * threads at once are safe, on one stream or on several. */
+ * threads at once are safe, on one stream or on several.
+ * Graph capture: a call on a stream that is being captured returns
+ * GEMM_ERR_WORKSPACE if its plan needs a workspace (a later call could free
+ * or replace the library-owned one while the graph still holds its address);
+ * use gemm_f16_f32_abt_ws with a caller workspace inside captured regions.
+ * Plans without a workspace (data-parallel, aligned operands) capture as
+ * they are. */
 gemm_status_t gemm_f16_f32_abt(int64_t M, int64_t N, int64_t K,
                                const void* A, int64_t lda,
                                const void* B, int64_t ldb,
@@ -112,8 +125,9 @@ gemm_status_t gemm_bf16_f32_abt_ws(int64_t M, int64_t N, int64_t K,
 const char* gemm_status_string(gemm_status_t s);
 
 /* Writes a one-line description of the plan chosen for (M, N, K) on a
- * 256-CU device (a whole MI355X) into the host buffer buf (NUL-terminated,
- * truncated to len). Touches no device.
+ * 256-CU device (a whole MI355X, unless the plan override names another CU
+ * count) into the host buffer buf (NUL-terminated, truncated to len).
+ * Touches no device.
  * Same size limits as gemm_f16_f32_abt (GEMM_ERR_NOT_SUPPORTED beyond them). */
 gemm_status_t gemm_f16_f32_abt_describe(int64_t M, int64_t N, int64_t K, char* buf, size_t len);
 
@@ -146,6 +160,32 @@ int64_t gemm_f16_schedule_dump(int64_t M, int64_t N, int64_t K, int64_t grid,
  * that the fragment reads (ds_read_b128) meet no LDS bank conflicts. */
 int32_t gemm_f16_lds_chunk(int32_t chunks_per_row, int32_t block_dim, int32_t row,
                            int32_t chunk);
+
+/* Plan override for tests and experiments (host only; no device is touched).
+ * `text` is a comma-separated list of key=integer pairs, any subset of
+ *   kid=<tiled kernel id>  mode=<0 data-parallel, 1 split-K, 2 stream-K,
+ *   3 whole data-parallel rounds then stream-K>  splits=<k-shares per tile>
+ *   grid=<workgroups>  group=<tile rows per band>  xcd=<0|1 renumbering>
+ *   cus=<compute units to plan for>  general=1 (the general kernel);
+ * keys the shape does not allow are ignored, so every plan stays correct.
+ * NULL or "" restores the default rule. The override applies to every later
+ * call in the process (all threads) and empties the plan cache. At first use
+ * the library takes its initial value from the environment variable
+ * GEMM_F16_PLAN; later changes to that variable are not read. */
+void gemm_f16_set_plan_override(const char* text);
+
+/* Clock probe for measurement (host only; nothing is launched). With
+ * `counters` a device pointer to two unsigned 64-bit integers, every later
+ * launch of a tiled main kernel (any host thread, any stream) has its first
+ * wave of workgroup 0 add, with device-scope atomics, the shader-clock cycles
+ * (s_memtime) to counters[0] and the 100 MHz real-time ticks (s_memrealtime)
+ * to counters[1] between the workgroup's start and its end. Over a set of
+ * launches, 100 MHz * counters[0] / counters[1] is then the average shader
+ * clock while they ran, which is what the MFMA peak scales with. The caller
+ * zeroes the counters, keeps them alive while such launches are in flight,
+ * and passes NULL to turn the probe off (the default). The general and
+ * reduce kernels are not probed. */
+void gemm_f16_set_clock_probe(unsigned long long* counters);
 
 
 #ifdef __cplusplus

@@ -17,3 +17,18 @@ def oracle_lib():
     import oracle
 
     return oracle.load()
+
+
+@pytest.fixture(autouse=True)
+def _default_plan_rule():
+    """Every test starts and ends on the default plan rule (tests that force a
+    plan set the library's override themselves)."""
+    from dense_fp16_gemm_03_amd import gemm
+
+    def reset():
+        if gemm._lib is not None or os.path.exists(gemm.LIBRARY):
+            gemm.gemm_f16_set_plan_override("")
+
+    reset()
+    yield
+    reset()

@@ -40,14 +40,14 @@ def test_traffic_needs_the_current_source(tmp_path, monkeypatch):
     good.write_text(json.dumps({"8192^3": {"source_hash": bench.source_hash(),
                                            "bytes_per_launch": 123}}))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(good))
-    assert bench.traffic_for("8192^3", 1e-3) == 123
-    assert bench.traffic_for("1024^3", 1e-3) is None
+    assert bench.traffic_for("8192^3") == 123
+    assert bench.traffic_for("1024^3") is None
     stale = tmp_path / "stale.json"
     stale.write_text(json.dumps({"8192^3": {"source_hash": "0" * 16, "bytes_per_launch": 123}}))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(stale))
-    assert bench.traffic_for("8192^3", 1e-3) is None
+    assert bench.traffic_for("8192^3") is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
-    assert bench.traffic_for("8192^3", 1e-3) is None
+    assert bench.traffic_for("8192^3") is None
 
 
 def test_cpu_baseline_record():
@@ -59,3 +59,31 @@ def test_cpu_baseline_record():
     Ab = inputs.uniform_bf16(M, K, 1)
     Bb = inputs.uniform_bf16(N, K, 2)
     assert np.isfinite(bench.cpu_baseline(Ab, Bb, M, N, K, budget_s=0.05)["value"])
+
+
+def test_roofline_bound_per_config():
+    """256^3 and 1024^3 sit below the ridge (HBM-bound); the other three
+    workloads are MFMA-bound."""
+    bounds = {n: bench.roofline_time(*inputs.WORKLOADS[n])[1] for n in inputs.WORKLOADS}
+    assert bounds == {"256^3": "hbm", "1024^3": "hbm", "2048x2048x16384": "mfma",
+                      "1024x1024x65536": "mfma", "8192^3": "mfma"}
+    t, _ = bench.roofline_time(8192, 8192, 8192)
+    assert abs(t - 2.0 * 8192**3 / 2.5e15) < 1e-12
+    t, _ = bench.roofline_time(1024, 1024, 1024)
+    assert abs(t - (2.0 * 2 * 1024 * 1024 + 4.0 * 1024 * 1024) / 8e12) < 1e-15
+
+
+def test_clock_window_summary():
+    """The telemetry summary keeps only the samples inside the timed window
+    and reads the power-limit residency as the ratio of counter deltas."""
+    s = bench.ClockSampler.__new__(bench.ClockSampler)
+    s.samples = [(0.5, [2400] * 8, 900, 0, 0, 0),
+                 (1.0, [1600] * 8, 1400, 100, 1000, 5),
+                 (1.5, [1700, 1500] * 4, 1380, 500, 2000, 9),
+                 (3.0, [2400] * 8, 800, 600, 3000, 12)]
+    w = s.window(0.9, 2.0)
+    assert w["samples"] == 2
+    assert w["gfx_clk_mhz_mean"] == 1600.0
+    assert w["gfx_clk_mhz_per_xcd"] == [1650.0, 1550.0] * 4
+    assert w["ppt_limited_frac"] == 0.4  # (500 - 100) / (2000 - 1000)
+    assert s.window(5.0, 6.0) is None

@@ -40,7 +40,7 @@ def log(msg):
 
 @pytest.fixture(autouse=True)
 def _each(request, monkeypatch):
-    monkeypatch.delenv("GEMM_F16_PLAN", raising=False)
+    gemm.gemm_f16_set_plan_override("")
     log(f"[gpu test] {request.node.name}")
     yield
     torch.cuda.synchronize()
@@ -116,11 +116,11 @@ def test_tall_c_beyond_2gib(plan, monkeypatch):
     if plan in ("packed", "general"):
         B = misaligned(B_host)  # packed into aligned rows, or the general kernel
         if plan == "general":
-            monkeypatch.setenv("GEMM_F16_PLAN", "general=1")
+            gemm.gemm_f16_set_plan_override("general=1")
     else:
         B = torch.from_numpy(B_host).to(DEV)
         if plan != "default":
-            monkeypatch.setenv("GEMM_F16_PLAN", plan)
+            gemm.gemm_f16_set_plan_override(plan)
     log(f"  plan: {plan_text(M, N, K, plan)} ({plan})")
     C = nan_c(M, N)
     gemm.gemm_abt(A, B, C)
@@ -184,7 +184,7 @@ def test_row_stride_at_offset_limit(monkeypatch):
     ld_in = ((2**31 - 1 - (K + 32) * 2) // (255 * 2)) // 8 * 8
     for ld, expect in ((ld_in, "tiled"), (ld_in + 8, "packed"), (ld_in + 8, "general")):
         if expect == "general":
-            monkeypatch.setenv("GEMM_F16_PLAN", "general=1")
+            gemm.gemm_f16_set_plan_override("general=1")
         A = inputs.device_uniform(M, K, 531, DEV, ld=ld)
         B = inputs.device_uniform(N, K, 532, DEV, ld=ld)
         log(f"  ld={ld} ({expect}; A and B {2 * M * ld / 2**30:.2f} GiB each)")
@@ -209,7 +209,7 @@ def test_m_at_index_limit(path, monkeypatch):
     if path in ("packed", "general"):
         B = misaligned(B_host)
         if path == "general":
-            monkeypatch.setenv("GEMM_F16_PLAN", "general=1")
+            gemm.gemm_f16_set_plan_override("general=1")
     else:
         B = torch.from_numpy(B_host).to(DEV)
     log(f"  plan: {plan_text(M, N, K, path)} ({path})")

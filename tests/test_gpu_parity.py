@@ -89,7 +89,7 @@ def assert_tol(got, ref, S, what):
 
 @pytest.fixture(autouse=True)
 def _name(request, monkeypatch):
-    monkeypatch.delenv("GEMM_F16_PLAN", raising=False)
+    gemm.gemm_f16_set_plan_override("")
     log(f"[gpu test] {request.node.name}")
     yield
 
@@ -247,7 +247,7 @@ def test_general_kernel_odd_k(M, N, K, force, monkeypatch):
     """The general kernel: small products with K % 8 != 0 take it by the plan
     rule; a larger one is forced onto it (it would otherwise be packed)."""
     if force:
-        monkeypatch.setenv("GEMM_F16_PLAN", "general=1")
+        gemm.gemm_f16_set_plan_override("general=1")
     assert "general" in gemm.gemm_f16_f32_abt_describe(M, N, K)
     A = inputs.uniform(M, K, 111)
     B = inputs.uniform(N, K, 112)
@@ -261,7 +261,7 @@ def test_strided_and_unaligned_views(plan, monkeypatch):
     packed into aligned copies by default and run on the general kernel when
     forced."""
     if plan:
-        monkeypatch.setenv("GEMM_F16_PLAN", plan)
+        gemm.gemm_f16_set_plan_override(plan)
     M, N, K = 300, 200, 256
     Abig = to_dev(inputs.integer(M, K + 24, 121))
     Bbig = to_dev(inputs.integer(N, K + 40, 122))
@@ -354,39 +354,34 @@ def test_subnormal_inputs():
 
 # --- every kernel variant and schedule mode ---------------------------------
 
-# Tiled kernel ids 0-9 use v_mfma_f32_32x32x16_f16, 10-24 v_mfma_f32_16x16x32_f16;
-# 25-29 run the ping-pong main loop (28 with the 32x32x16 MFMA); 30-34 are
-# small tiles with deep rings; 35 is the ping-pong loop over two 64-wide stages.
-PLANS = [f"kid={k}" for k in range(36)] + [
-    "kid=0,mode=1,splits=3", "kid=0,mode=2", "kid=0,mode=2,grid=37",
-    "kid=4,mode=2,grid=100", "kid=6,mode=1,splits=5", "kid=2,mode=2,grid=64",
-    "kid=1,mode=1,splits=2", "kid=3,mode=2,grid=29", "kid=5,mode=2,grid=130",
-    "kid=7,mode=1,splits=4", "kid=9,mode=2", "kid=4,mode=1,splits=3,grid=40",
-    "kid=10,mode=1,splits=3", "kid=12,mode=2,grid=37", "kid=15,mode=2,grid=29",
-    "kid=11,mode=1,splits=2", "kid=19,mode=2", "kid=16,mode=1,splits=3,grid=40",
-    "kid=14,mode=2,grid=64", "kid=18,mode=1,splits=5", "kid=20,mode=1,splits=3",
-    "kid=21,mode=2,grid=37", "kid=22,mode=2", "kid=24,mode=1,splits=2",
-    "kid=25,mode=1,splits=3", "kid=26,mode=2,grid=37", "kid=27,mode=2",
-    "kid=28,mode=1,splits=2,grid=40", "kid=29,mode=2,grid=29",
-    "kid=30,mode=1,splits=3", "kid=31,mode=2,grid=37", "kid=32,mode=2",
+# The kernels built: 16 (128x128x64) and 18 (64x64x64) run the symmetric
+# tiled loop; 27 (32-wide three-stage ring) and 28 (its 32x32x16 form, five
+# stages) the ping-pong loop; 35 and 36 (its 32x32x16 form) the ping-pong loop
+# over two 64-wide stages. Every one under every schedule mode.
+KIDS = [16, 18, 27, 28, 35, 36]
+PLANS = [f"kid={k}" for k in KIDS] + [
+    "kid=16,mode=1,splits=3", "kid=16,mode=2", "kid=16,mode=2,grid=37",
+    "kid=16,mode=1,splits=3,grid=40", "kid=18,mode=1,splits=5", "kid=18,mode=2,grid=130",
+    "kid=27,mode=1,splits=4", "kid=27,mode=2", "kid=27,mode=2,grid=29",
+    "kid=28,mode=1,splits=2,grid=40", "kid=28,mode=2,grid=37",
+    "kid=36,mode=1,splits=3", "kid=36,mode=2,grid=29",
     # Several units per workgroup: the ping-pong kernels start the next unit's
     # loads before the previous unit's stores, mixing full tiles (vector
     # stores left in flight) with ragged ones (element stores).
-    "kid=25,grid=2", "kid=26,grid=3", "kid=27,grid=3", "kid=27,grid=1",
-    "kid=27,mode=1,splits=2,grid=7", "kid=28,grid=4", "kid=29,grid=5",
+    "kid=27,grid=3", "kid=27,grid=1", "kid=27,mode=1,splits=2,grid=7", "kid=28,grid=4",
     "kid=35,grid=1", "kid=35,grid=3", "kid=35,mode=1,splits=2,grid=7", "kid=35,mode=1,splits=3",
-    "kid=35,mode=2", "kid=35,mode=2,grid=37",
+    "kid=35,mode=2", "kid=35,mode=2,grid=37", "kid=36,grid=1", "kid=36,grid=3",
+    "kid=36,mode=1,splits=2,grid=7",
     # Whole data-parallel rounds, then stream-K over the tiles left (the
     # forced grids make whole rounds at this size).
-    "kid=27,mode=3,grid=4", "kid=26,mode=3,grid=5", "kid=16,mode=3,grid=7",
-    "kid=18,mode=3,grid=50", "kid=4,mode=3,grid=11", "kid=29,mode=3,grid=8",
-    "kid=35,mode=3,grid=4",
+    "kid=27,mode=3,grid=4", "kid=16,mode=3,grid=7", "kid=18,mode=3,grid=50",
+    "kid=28,mode=3,grid=5", "kid=35,mode=3,grid=4", "kid=36,mode=3,grid=4",
 ]
 
 
 @pytest.mark.parametrize("plan", PLANS)
 def test_forced_plans(plan, monkeypatch):
-    monkeypatch.setenv("GEMM_F16_PLAN", plan)
+    gemm.gemm_f16_set_plan_override(plan)
     M, N, K = 600, 520, 1352
     log(f"  plan: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
     Ai = inputs.integer(M, K, 131)
@@ -399,12 +394,12 @@ def test_forced_plans(plan, monkeypatch):
     assert_tol(run(A, B), ref, S, f"{plan} uniform")
 
 
-@pytest.mark.parametrize("kid", [0, 7, 10, 11, 12, 19, 20, 22, 23, 25, 27, 29, 30, 31, 35])
+@pytest.mark.parametrize("kid", KIDS)
 @pytest.mark.parametrize("K", [24, 72, 200])
 def test_forced_plans_short_k(kid, K, monkeypatch):
     """K of one to a few k-tiles, odd and even counts (one k-step per stage
     runs its stages in pairs plus a tail)."""
-    monkeypatch.setenv("GEMM_F16_PLAN", f"kid={kid}")
+    gemm.gemm_f16_set_plan_override(f"kid={kid}")
     M, N = 300, 264
     Ai, Bi = inputs.integer(M, K, 151), inputs.integer(N, K, 152)
     ref, _ = oracle.gemm_abt(Ai, Bi)
@@ -414,14 +409,15 @@ def test_forced_plans_short_k(kid, K, monkeypatch):
     assert_tol(run(A, B), ref, S, f"kid={kid} K={K} uniform")
 
 
-@pytest.mark.parametrize("plan", ["kid=25,grid=1", "kid=26,grid=2", "kid=27,grid=1",
+@pytest.mark.parametrize("plan", ["kid=28,grid=1", "kid=28,grid=2", "kid=27,grid=1",
                                   "kid=27,mode=1,splits=2,grid=3", "kid=35,grid=1",
-                                  "kid=35,grid=2", "kid=35,mode=1,splits=2,grid=3"])
+                                  "kid=35,grid=2", "kid=35,mode=1,splits=2,grid=3",
+                                  "kid=36,grid=2"])
 @pytest.mark.parametrize("K", [24, 72, 200])
 def test_forced_plans_short_units(plan, K, monkeypatch):
     """Many short units per workgroup: units of one to a few k-tiles follow
     each other while the previous unit's stores may still be in flight."""
-    monkeypatch.setenv("GEMM_F16_PLAN", plan)
+    gemm.gemm_f16_set_plan_override(plan)
     M, N = 776, 520
     log(f"  plan: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
     Ai, Bi = inputs.integer(M, K, 155), inputs.integer(N, K, 156)
@@ -464,6 +460,93 @@ def test_repeat_and_caller_workspace(name):
     ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device=DEV)
     for _ in range(2):
         assert np.array_equal(first, run(At, Bt, workspace=ws))
+
+
+def test_repeat_full_size_default_plan():
+    """8192^3 on its default plan (several units per workgroup, each unit's C
+    stores left in flight while the next unit's loads start): two calls on
+    uniform inputs and two on hash-integer inputs give the same C bit for bit
+    over all 67 million elements, and each input kind matches the reference
+    at sampled rows, columns and points (exactly on the integers)."""
+    M, N, K = WORKLOADS["8192^3"]
+    log(f"  plan: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
+    rows, cols = sample_points(M, N, n_rand=2000, seed=11)
+    for kind in ("uniform", "hash_int"):
+        A, B = operands((M, N, K), kind)
+        At, Bt = to_dev(A), to_dev(B)
+        first = run(At, Bt)
+        second = run(At, Bt, fill=-7.0)
+        same = first == second
+        assert same.all(), f"{kind}: {(~same).sum()} elements differ between two calls"
+        ref, S = oracle.gemm_abt_elems(A, B, rows, cols)
+        if kind == "hash_int":
+            assert_exact(first[rows, cols], ref, "8192^3 hash_int")
+        else:
+            assert_tol(first[rows, cols], ref, S, "8192^3 uniform")
+        del At, Bt, first, second
+        torch.cuda.empty_cache()
+
+
+def test_capture_needs_a_caller_workspace():
+    """A split plan called while its stream is being captured, without a
+    caller workspace, is refused (GEMM_ERR_WORKSPACE) before anything is
+    enqueued: the graph would otherwise keep the address of a library-owned
+    workspace a later call may free. A data-parallel plan captures as is."""
+    M, N, K = 512, 512, 8192  # split-K plan
+    assert "mode=split" in gemm.gemm_f16_f32_abt_describe(M, N, K)
+    A, B = operands((M, N, K), "integer")
+    At, Bt = to_dev(A), to_dev(B)
+    C = torch.full((M, N), np.nan, dtype=torch.float32, device=DEV)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(gemm.GemmError) as e:
+        with torch.cuda.graph(g, stream=s):
+            gemm.gemm_abt(At, Bt, C)
+    assert e.value.status == 5
+    torch.cuda.synchronize()
+    assert torch.isnan(C).all()  # nothing ran
+    ref, _ = oracle.gemm_abt(A, B)
+    assert_exact(run(At, Bt), ref, "split plan after the refused capture")
+
+
+@pytest.mark.parametrize("name", ["8192^3", "1024x1024x65536", "1024^3"])
+def test_clock_probe(name):
+    """The clock probe: with it on, C is bitwise the same; the counters hold
+    shader cycles and 100 MHz ticks whose ratio is a plausible clock, and
+    whose ticks agree with the event-timed duration of the probed kernels;
+    with it off, the counters no longer move."""
+    M, N, K = WORKLOADS[name]
+    A, B = operands((M, N, K), "integer")
+    At, Bt = to_dev(A), to_dev(B)
+    plain = run(At, Bt)
+    ctr = torch.zeros(2, dtype=torch.int64, device=DEV)
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    calls = 5
+    torch.cuda.synchronize()
+    gemm.gemm_f16_set_clock_probe(ctr.data_ptr())
+    try:
+        s.record()
+        for _ in range(calls):
+            gemm.gemm_abt(At, Bt, C)
+        e.record()
+        torch.cuda.synchronize()
+    finally:
+        gemm.gemm_f16_set_clock_probe(0)
+    assert np.array_equal(C.cpu().numpy(), plain)
+    cycles, ticks = (int(v) for v in ctr.tolist())
+    mhz = 100.0 * cycles / max(ticks, 1)
+    probed_us = ticks / 100.0
+    event_us = s.elapsed_time(e) * 1e3
+    log(f"  {name}: {mhz:.0f} MHz; probed {probed_us:.1f} us vs {event_us:.1f} us between events")
+    assert ticks > 0 and 200 <= mhz <= 2600
+    # workgroup 0 spans its main kernel; the events also hold the reduce pass
+    # and the gaps between calls (most of the time for the small shape)
+    assert 0.25 * event_us <= probed_us <= 1.05 * event_us
+    gemm.gemm_abt(At, Bt, C)
+    torch.cuda.synchronize()
+    assert [int(v) for v in ctr.tolist()] == [cycles, ticks]
 
 
 def test_non_default_stream():
