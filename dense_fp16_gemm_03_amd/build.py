@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libgemm_f16.so")
 ASM_DIR = os.path.join(ROOT, "_build")
-SOURCES = [os.path.join(CSRC, "gemm_kernels.hip"), os.path.join(CSRC, "gemm_api.cpp")]
+SOURCES = [os.path.join(CSRC, "gemm_kernels.hip"), os.path.join(CSRC, "gemm_api.cpp"),
+           os.path.join(CSRC, "gemm_noalloc.hip")]
 # hipBLASLt context arm (measurement only; see vendor/hipblaslt_arm.cpp).
 VENDOR_SOURCE = os.path.join(PKG, "vendor", "hipblaslt_arm.cpp")
 VENDOR_LIBRARY = os.path.join(PKG, "libvendor_hipblaslt.so")

@@ -473,23 +473,38 @@ Plan caller_plan(Plan plan, const void* ws, size_t ws_bytes) {
   return plan;
 }
 
+// Where a call's workspace comes from: the library's per-stream allocation,
+// the caller's buffer, or the static scratch array of the no-allocation
+// entry point.
+enum WsSource { WS_LIBRARY, WS_CALLER, WS_STATIC };
+
 gemm_status_t run(int32_t dt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                  const void* B, int64_t ldb, float* C, int64_t ldc, bool caller_ws, void* ws,
+                  const void* B, int64_t ldb, float* C, int64_t ldc, WsSource src, void* ws,
                   size_t ws_bytes, void* stream_v) {
   gemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc);
   if (st != GEMM_OK) return st;
   if (M == 0 || N == 0) return GEMM_OK;
   hipStream_t stream = (hipStream_t)stream_v;
+  const bool caller_ws = src != WS_LIBRARY;
   // One plan per call, for the CU count gemm_f16_f32_abt_workspace_size also
   // uses; the caller's workspace is checked against it before anything is
   // enqueued.
   const int dev = current_device();
   Plan plan = lookup_plan(M, N, K, A, lda, B, ldb, C, ldc, dt, dev);
-  if (caller_ws) {
+  if (src == WS_CALLER) {
     plan = caller_plan(plan, ws, ws_bytes);
     if (!workspace_fits(plan, ws, ws_bytes)) return GEMM_ERR_WORKSPACE;
+  } else if (src == WS_STATIC && plan.workspace > ws_bytes) {
+    // Packing is an optimisation (the general kernel needs no workspace);
+    // partial tiles beyond the scratch array are an error.
+    if (!(plan.pack_a || plan.pack_b)) return GEMM_ERR_SCRATCH;
+    Plan general;
+    general.kid = KID_GENERAL;
+    general.c_vec4 = plan.c_vec4;
+    plan = general;
   }
   if (dev < 0) return GEMM_ERR_HIP;
+  if (src == WS_STATIC && plan.workspace > 0 && ws == nullptr) return GEMM_ERR_HIP;
   if (plan.kid != KID_GENERAL && !tiled_has(plan.kid, dt)) return GEMM_ERR_NOT_SUPPORTED;
   if (plan.workspace > 0 && !caller_ws) {
     // A library-owned workspace can be freed and replaced by a later call on
@@ -554,16 +569,26 @@ gemm_status_t run(int32_t dt, int64_t M, int64_t N, int64_t K, const void* A, in
 
 }  // namespace
 
+namespace g16 {
+
+gemm_status_t run_in_scratch(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                             const void* B, int64_t ldb, float* C, int64_t ldc, void* scratch,
+                             size_t scratch_bytes, void* stream) {
+  return run(DT_F16, M, N, K, A, lda, B, ldb, C, ldc, WS_STATIC, scratch, scratch_bytes, stream);
+}
+
+}  // namespace g16
+
 extern "C" {
 
 gemm_status_t gemm_f16_f32_abt(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                                const void* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
-  return run(DT_F16, M, N, K, A, lda, B, ldb, C, ldc, false, nullptr, 0, stream);
+  return run(DT_F16, M, N, K, A, lda, B, ldb, C, ldc, WS_LIBRARY, nullptr, 0, stream);
 }
 
 gemm_status_t gemm_bf16_f32_abt(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                                 const void* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
-  return run(DT_BF16, M, N, K, A, lda, B, ldb, C, ldc, false, nullptr, 0, stream);
+  return run(DT_BF16, M, N, K, A, lda, B, ldb, C, ldc, WS_LIBRARY, nullptr, 0, stream);
 }
 
 size_t gemm_f16_f32_abt_workspace_size(int64_t M, int64_t N, int64_t K) {
@@ -582,7 +607,8 @@ size_t gemm_f16_f32_abt_workspace_size(int64_t M, int64_t N, int64_t K) {
 gemm_status_t gemm_f16_f32_abt_ws(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                                   const void* B, int64_t ldb, float* C, int64_t ldc,
                                   void* workspace, size_t workspace_bytes, void* stream) {
-  return run(DT_F16, M, N, K, A, lda, B, ldb, C, ldc, true, workspace, workspace_bytes, stream);
+  return run(DT_F16, M, N, K, A, lda, B, ldb, C, ldc, WS_CALLER, workspace, workspace_bytes,
+             stream);
 }
 
 size_t gemm_bf16_f32_abt_workspace_size(int64_t M, int64_t N, int64_t K) {
@@ -593,7 +619,8 @@ size_t gemm_bf16_f32_abt_workspace_size(int64_t M, int64_t N, int64_t K) {
 gemm_status_t gemm_bf16_f32_abt_ws(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                                    const void* B, int64_t ldb, float* C, int64_t ldc,
                                    void* workspace, size_t workspace_bytes, void* stream) {
-  return run(DT_BF16, M, N, K, A, lda, B, ldb, C, ldc, true, workspace, workspace_bytes, stream);
+  return run(DT_BF16, M, N, K, A, lda, B, ldb, C, ldc, WS_CALLER, workspace, workspace_bytes,
+             stream);
 }
 
 const char* gemm_status_string(gemm_status_t s) {
@@ -604,6 +631,9 @@ const char* gemm_status_string(gemm_status_t s) {
     case GEMM_ERR_HIP: return "GEMM_ERR_HIP: a HIP runtime call failed";
     case GEMM_ERR_ALLOC: return "GEMM_ERR_ALLOC: workspace allocation failed";
     case GEMM_ERR_WORKSPACE: return "GEMM_ERR_WORKSPACE: workspace too small or misaligned";
+    case GEMM_ERR_SCRATCH:
+      return "GEMM_ERR_SCRATCH: the plan needs more workspace than the static scratch array "
+             "of gemm_f16_f32_abt_noalloc holds";
     default: return "unknown gemm_status_t";
   }
 }

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gemm_f16.h"
 #include "gemm_schedule.h"
 
 namespace g16 {
@@ -87,6 +88,14 @@ hipError_t launch_general(int32_t dt, const GemmParams& p, hipStream_t stream);
 // 16-byte aligned), zero-filling elements K .. kp - 1.
 hipError_t launch_pack(const uint16_t* src, int64_t ld, int32_t K, int64_t rows, int32_t kp,
                        void* dst, hipStream_t stream);
+
+// The binary16 entry point's path with its workspace in `scratch` (a device
+// buffer of scratch_bytes the library does not allocate; NULL where no device
+// is current). A plan whose partial tiles need more returns GEMM_ERR_SCRATCH;
+// operands that would be packed into more run the general kernel.
+gemm_status_t run_in_scratch(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                             const void* B, int64_t ldb, float* C, int64_t ldc, void* scratch,
+                             size_t scratch_bytes, void* stream);
 
 // Workgroups of kernel `kid` that fit on one CU at once (0 on error).
 int32_t tiled_occupancy(int32_t kid);

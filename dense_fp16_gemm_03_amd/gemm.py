@@ -17,7 +17,7 @@ LIBRARY = os.path.join(PKG, "libgemm_f16.so")
 GEMM_OK = 0
 STATUS_NAMES = {
     0: "GEMM_OK", 1: "GEMM_ERR_INVALID_VALUE", 2: "GEMM_ERR_NOT_SUPPORTED",
-    3: "GEMM_ERR_HIP", 4: "GEMM_ERR_ALLOC", 5: "GEMM_ERR_WORKSPACE",
+    3: "GEMM_ERR_HIP", 4: "GEMM_ERR_ALLOC", 5: "GEMM_ERR_WORKSPACE", 6: "GEMM_ERR_SCRATCH",
 }
 
 # Every symbol include/gemm_f16.h declares.
@@ -27,6 +27,7 @@ EXPORTS = (
     "gemm_f16_schedule_dump", "gemm_f16_lds_chunk", "gemm_bf16_f32_abt",
     "gemm_bf16_f32_abt_workspace_size",
     "gemm_bf16_f32_abt_ws", "gemm_f16_set_plan_override", "gemm_f16_set_clock_probe",
+    "gemm_f16_f32_abt_noalloc",
 )
 
 _lib = None
@@ -55,6 +56,8 @@ def load(path: str = LIBRARY):
     lib.gemm_f16_f32_abt_workspace_size.restype = sz
     lib.gemm_f16_f32_abt_ws.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, sz, p]
     lib.gemm_f16_f32_abt_ws.restype = st
+    lib.gemm_f16_f32_abt_noalloc.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
+    lib.gemm_f16_f32_abt_noalloc.restype = st
     lib.gemm_bf16_f32_abt.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
     lib.gemm_bf16_f32_abt.restype = st
     lib.gemm_bf16_f32_abt_workspace_size.argtypes = [i64, i64, i64]
@@ -97,6 +100,12 @@ def gemm_f16_f32_abt_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_by
                         stream=0) -> int:
     return load().gemm_f16_f32_abt_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace,
                                       workspace_bytes, stream)
+
+
+def gemm_f16_f32_abt_noalloc(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    """Raw call with the workspace in the library's static scratch array;
+    returns the status code (does not raise)."""
+    return load().gemm_f16_f32_abt_noalloc(M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
 def gemm_f16_f32_abt_workspace_size(M, N, K) -> int:

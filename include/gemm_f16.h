@@ -45,7 +45,8 @@ typedef enum {
   GEMM_ERR_NOT_SUPPORTED = 2, /* shape/alignment outside what any kernel here handles */
   GEMM_ERR_HIP = 3,           /* a HIP runtime call failed (launch, allocation of events...) */
   GEMM_ERR_ALLOC = 4,         /* library-owned workspace could not be allocated */
-  GEMM_ERR_WORKSPACE = 5      /* caller workspace too small or misaligned */
+  GEMM_ERR_WORKSPACE = 5,     /* caller workspace too small or misaligned */
+  GEMM_ERR_SCRATCH = 6        /* gemm_f16_f32_abt_noalloc: plan needs more than its scratch */
 } gemm_status_t;
 
 /* C = A * B^T (see the layout block above). A, B, C are device pointers.
@@ -120,6 +121,29 @@ gemm_status_t gemm_bf16_f32_abt_ws(int64_t M, int64_t N, int64_t K,
                                    const void* B, int64_t ldb,
                                    float* C, int64_t ldc,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. As
+ * gemm_f16_f32_abt, but every workspace the call needs (split-K and stream-K
+ * partial tiles, packed operands) lives in a static device array of 64 MiB
+ * (67108864 bytes) inside the library, so the call never allocates or frees
+ * memory (no hipMalloc, no hipFree). Each device the entry point runs on
+ * holds its own copy of the array from the first call on it until the
+ * process ends; its address is looked up once per device with
+ * hipGetSymbolAddress. The array covers every split-K plan and the five
+ * reference workloads; a plan whose partial tiles need more returns
+ * GEMM_ERR_SCRATCH before anything is enqueued (operands that would be packed
+ * into more run the general kernel instead). Nothing in the array needs to
+ * start at zero and it keeps the last call's contents. All calls on one
+ * device share the one array: calls that can overlap in time on one device
+ * (on different streams, or from threads without ordering) race and corrupt
+ * each other's results; order them on one stream. Calls are safe to capture
+ * in a HIP graph. Same arguments, layouts and other errors as
+ * gemm_f16_f32_abt (binary16 operands). */
+gemm_status_t gemm_f16_f32_abt_noalloc(int64_t M, int64_t N, int64_t K,
+                                       const void* A, int64_t lda,
+                                       const void* B, int64_t ldb,
+                                       float* C, int64_t ldc, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* gemm_status_string(gemm_status_t s);

@@ -86,6 +86,16 @@ def test_bf16_workspace_and_dtype_checks(lib):
         gemm.gemm_abt(torch.zeros(2, 2), torch.zeros(2, 2))
 
 
+def test_noalloc_checks_without_a_device(lib):
+    """The no-allocation entry point reports argument errors and plans beyond
+    its 64 MiB scratch before it needs a device."""
+    assert gemm.gemm_f16_f32_abt_noalloc(-1, 4, 4, A_PTR, 4, B_PTR, 4, C_PTR, 4, 0) == 1
+    assert gemm.gemm_f16_f32_abt_noalloc(4, 4, 8, A_PTR, 8, B_PTR, 8, A_PTR + 16, 4, 0) == 1
+    assert gemm.gemm_f16_f32_abt_noalloc(0, 4, 8, A_PTR, 8, B_PTR, 8, C_PTR, 4, 0) == 0
+    M, N, K = 4352, 4352, 4096  # 74.25 MiB of partial tiles
+    assert gemm.gemm_f16_f32_abt_noalloc(M, N, K, A_PTR, K, 1 << 40, K, 1 << 44, N, 0) == 6
+
+
 def test_caller_workspace_checked_first(lib):
     M, N, K = inputs.WORKLOADS["1024x1024x65536"]
     need = gemm.gemm_f16_f32_abt_workspace_size(M, N, K)
