@@ -26,12 +26,13 @@ constexpr int32_t kDefaultCUs = 256;  // MI355X: 8 XCDs x 32 CUs
 // integers, and a tile's first index plus its extent (at most 256, plus the
 // ring's masked tail stages in k) must not pass 2^31 - 1.
 constexpr int64_t kMaxDim = 0x7FFFFFFF - 1024;
-// Kernel for large squares and for long K: 256x256 tiles, 16x16x32 MFMA,
-// two waves per SIMD in the ping-pong main loop.
+// Kernel for large tiles with K below 4096: 256x256 tiles, 16x16x32 MFMA,
+// two waves per SIMD in the ping-pong main loop over a 32-wide ring.
 constexpr int32_t KID_LARGE = KID_256x256x32_S3_W8_M16_PP;
-// The same tiles over two 64-wide stages (whole 128-byte rows per load): for
-// at least a round of tiles with K >= 4096.
-constexpr int32_t KID_LARGE64 = KID_256x256x64_S2_W8_M16_PP;
+// The same tiles over 64-wide stages (whole 128-byte rows per load) held as
+// A and B halves in five LDS slots: for at least a round of tiles with
+// K >= 4096, and for long K split over the CUs.
+constexpr int32_t KID_LARGE64 = KID_256x256x64_H5_W8_M16_PP;
 
 // Whether the tiles left after whole data-parallel rounds of 256x256 tiles
 // are shared by stream-K (see make_plan).
@@ -153,9 +154,10 @@ bool tiled_eligible(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
 // set from measurements on the MI355X:
 //   * at least one 256x256 tile per CU: 256x256 tiles, data-parallel,
 //     persistent grid walking the tiles by stride; with K >= 4096 the main
-//     loop over 64-wide stages;
-//   * fewer tiles but long K (>= 128 k-steps of 32): the same tiles with K
-//     split so tiles x splits fills the CUs (each share keeps >= 64 k-steps);
+//     loop over 64-wide stages in five half-stage slots;
+//   * fewer tiles but long K (>= 128 k-steps of 32): the same tiles and main
+//     loop with K split so tiles x splits fills the CUs (each share keeps
+//     >= 64 k-steps of 32);
 //   * smaller problems: 128x128 tiles, or 64x64 tiles when 128x128 ones
 //     would fill fewer than half the CUs, data-parallel (at these sizes the
 //     reduce pass of a split costs more than it gains);
@@ -234,7 +236,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
     if (t256 >= cus) {
       kid = k32 >= 128 ? KID_LARGE64 : KID_LARGE;
     } else if (k32 >= 128) {
-      kid = KID_LARGE;
+      kid = KID_LARGE64;
       int64_t sp = cus / t256;
       if (sp > k32 / 64) sp = k32 / 64;  // each share keeps >= 64 k-steps of 32
       splits = (int32_t)std::max<int64_t>(sp, 1);

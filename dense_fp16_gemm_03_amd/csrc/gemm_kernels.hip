@@ -165,7 +165,9 @@ struct Cfg {
   static constexpr int A_BYTES = BM * ROW_BYTES;
   static constexpr int B_BYTES = BN * ROW_BYTES;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = STAGE_BYTES * STAGES;
+  // PP 3 keeps the A and B halves of its 64-wide stages in STAGES separate
+  // slots of one half each (gemm_pingpong_ring_kernel).
+  static constexpr int LDS_BYTES = PP == 3 ? A_BYTES * STAGES : STAGE_BYTES * STAGES;
   static constexpr int A_LOADS = BM / RPL / WAVES;    // per wave per stage
   static constexpr int B_LOADS = BN / RPL / WAVES;
   static constexpr int LOADS = A_LOADS + B_LOADS;
@@ -1069,6 +1071,175 @@ void gemm_pingpong64_kernel(GemmParams p) {
   probe_end(p, probe, lane);
 }
 
+// Fragments of the A tile (all FM blocks of the wave) or of the B tile (all
+// FN blocks) for MFMA k-step ks, from an LDS slot holding that tile alone.
+template <class C>
+__device__ __forceinline__ void read_a_frags(const char* slot, int ks, int wm, int lane,
+                                             typename C::M::frag_t (&a)[C::FM]) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+    a[i] = *reinterpret_cast<const typename C::M::frag_t*>(
+        slot + frag_off<C>(wm * C::WM + i * C::M::DIM, ks, lane));
+}
+
+template <class C>
+__device__ __forceinline__ void read_b_frags(const char* slot, int ks, int wn, int lane,
+                                             typename C::M::frag_t (&b)[C::FN]) {
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j)
+    b[j] = *reinterpret_cast<const typename C::M::frag_t*>(
+        slot + frag_off<C>(wn * C::WN + j * C::M::DIM, ks, lane));
+}
+
+// This wave's loads of the A (or B) half of the stage whose first k is k0,
+// into an LDS slot holding that half alone.
+template <class C>
+__device__ __forceinline__ void issue_a_half(char* slot, const UnitLoads<C>& u, int wave, int k0) {
+#pragma unroll
+  for (int j = 0; j < C::A_LOADS; ++j) {
+    const uint32_t off = k0 < u.ma.lim[j] ? u.ma.off[j] : kMaskedOffset;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        u.op.ra, (lds_void_ptr)(slot + (wave * C::A_LOADS + j) * 1024), 16, off, k0 * 2, 0, 0);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void issue_b_half(char* slot, const UnitLoads<C>& u, int wave, int k0) {
+#pragma unroll
+  for (int j = 0; j < C::B_LOADS; ++j) {
+    const uint32_t off = k0 < u.mb.lim[j] ? u.mb.off[j] : kMaskedOffset;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        u.op.rb, (lds_void_ptr)(slot + (wave * C::B_LOADS + j) * 1024), 16, off, k0 * 2, 0, 0);
+  }
+}
+
+// Ping-pong main loop over 64-wide stages held as separate A and B halves in
+// five LDS slots of 32 KiB (the whole 160 KiB), with the same two wave groups
+// and phases as gemm_pingpong64_kernel (one memory and one compute phase per
+// 32-wide k-step). The memory phase of a stage's first k-step reads the B
+// fragments of both its k-steps (and the A fragments of the first), so the
+// stage's B half is free after both groups' first memory phase and its A half
+// after their second. Stage s takes A slot 2 (s mod 3) and B slot
+// 1 + 2 (s mod 2), so each half of stage s + 2 goes into the slot its
+// counterpart of stage s - 1 (A) or s (B) has just freed:
+//   k-step 0 of stage it: read A(it) k-step 0 and B(it) both k-steps; issue
+//     this wave's loads of A(it + 2) into A(it - 1)'s slot;
+//   k-step 1 of stage it: read A(it) k-step 1; issue B(it + 2) into
+//     B(it)'s slot; wait until stage it + 1 has landed (group 1 here, group 0
+//     after its compute phase, both before the barrier that opens stage
+//     it + 1).
+// A half is thus awaited four to seven phases after it was issued, where the
+// two-stage loop of gemm_pingpong64_kernel awaits a stage two phases after
+// issuing it. In steady state the loads younger than an awaited stage are
+// exactly the next stage's A and B halves (LOADS). Units run one after
+// another: the ring drains (masked tail stages) and every wave's stores are
+// issued before the next unit's first loads.
+template <class C>
+__global__ __launch_bounds__(C::THREADS)
+__attribute__((amdgpu_waves_per_eu(C::WAVES_PER_EU, C::WAVES_PER_EU)))
+void gemm_pingpong_ring_kernel(GemmParams p) {
+  static_assert(C::WAVES == 8, "ping-pong pairs two waves per SIMD");
+  static_assert(C::BK == 64 && C::KSTEPS == 2 && C::STAGES == 5 && C::A_BYTES == C::B_BYTES,
+                "five half-stage slots of 64-wide stages, one k-step per phase");
+  constexpr int SLOT = C::A_BYTES;
+  constexpr int kRing = C::LOADS;  // loads younger than an awaited stage
+  typedef typename C::M::frag_t frag_t;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool late = wave >= 4;  // group 1
+  const int wm = wave / C::WGN;
+  const int wn = wave % C::WGN;
+  const int v = virtual_wg(blockIdx.x, p.s.grid, p.s.xcd_remap);
+  const ClockProbe probe = probe_start(p, wave);
+
+  Segment seg;
+  for (int n = 0; seg_at_uniform(p.s, v, n, &seg); ++n) {
+    UnitLoads<C> u;
+    unit_loads<C>(p, seg, wave, lane, u);
+    typename C::acc_t acc[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) acc[i][j] = typename C::acc_t{};
+
+    // The previous unit's loads (its masked tail) and stores are done and no
+    // wave reads the slots any more.
+    wait_vm<0>();
+    wait_lgkm_zero();
+    phase_barrier();
+    // Stages 0 and 1 into slots 0-3; stage 0 awaited.
+    issue_a_half<C>(smem, u, wave, u.k_begin * C::BK);
+    issue_b_half<C>(smem + SLOT, u, wave, u.k_begin * C::BK);
+    issue_a_half<C>(smem + 2 * SLOT, u, wave, (u.k_begin + 1) * C::BK);
+    issue_b_half<C>(smem + 3 * SLOT, u, wave, (u.k_begin + 1) * C::BK);
+    wait_vm<kRing>();
+    phase_barrier();
+    if (late) phase_barrier();  // group 1 starts one phase behind
+
+    frag_t fa[C::FM], fb0[C::FN], fb1[C::FN];
+    int ia = 0, ib = 0;  // it mod 3, it mod 2
+    for (int it = 0; it < u.nk; ++it) {
+      const char* sa = smem + 2 * ia * SLOT;
+      char* sb = smem + (1 + 2 * ib) * SLOT;
+      char* sa_next = smem + 2 * (ia == 0 ? 2 : ia - 1) * SLOT;  // slot of A(it - 1) = A(it + 2)
+      const int k_next = (u.k_begin + it + 2) * C::BK;
+      // Memory phase, k-step 0.
+      read_a_frags<C>(sa, 0, wm, lane, fa);
+      read_b_frags<C>(sb, 0, wn, lane, fb0);
+      read_b_frags<C>(sb, 1, wn, lane, fb1);
+      issue_a_half<C>(sa_next, u, wave, k_next);
+      wait_lgkm_zero();
+      phase_barrier();
+      // Compute phase, k-step 0 (serpentine order, as in gemm_pingpong_kernel).
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < C::FN; ++jj) {
+          const int j = (i & 1) ? C::FN - 1 - jj : jj;
+          acc[i][j] = C::M::mma(fb0[j], fa[i], acc[i][j]);
+        }
+      phase_barrier();
+      // Memory phase, k-step 1: both groups have read B(it), so its slot
+      // takes B(it + 2).
+      read_a_frags<C>(sa, 1, wm, lane, fa);
+      issue_b_half<C>(sb, u, wave, k_next);
+      if (late) wait_vm<kRing>();
+      wait_lgkm_zero();
+      phase_barrier();
+      // Compute phase, k-step 1.
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < C::FN; ++jj) {
+          const int j = (i & 1) ? C::FN - 1 - jj : jj;
+          acc[i][j] = C::M::mma(fb1[j], fa[i], acc[i][j]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      if (!late) wait_vm<kRing>();
+      phase_barrier();
+      ia = ia == 2 ? 0 : ia + 1;
+      ib ^= 1;
+    }
+
+    // Group 0 is here while group 1 runs its last compute phase.
+    const int m_base = u.m0 + wm * C::WM;
+    const int n_base = u.n0 + wn * C::WN;
+    if (seg.role == ROLE_ONLY) {
+      epilogue_stream<C>(p, acc, m_base, n_base, lane);
+    } else {
+      write_partial<C>(p.partials + ((int64_t)(seg.tile - p.s.shared_base) * p.s.slots + seg.index) *
+                                        (C::BM * C::BN / 4),
+                       acc, wave, lane);
+    }
+    // Matches group 1's extra barrier at the start of the unit.
+    if (!late) phase_barrier();
+  }
+  probe_end(p, probe, lane);
+}
+
 // Shares of output tile t under schedule s (1: the tile was stored directly).
 __device__ __forceinline__ int tile_shares(const Sched& s, int t) {
   if (s.mode == MODE_SPLIT) return s.splits;
@@ -1207,10 +1378,14 @@ constexpr KernelInfo kInfo27 = info_of<K27>("256x256x32_s3_w8_m16_pp");
 constexpr KernelInfo kInfo28 = info_of<K28>("256x256x32_s5_w8_pp");
 constexpr KernelInfo kInfo35 = info_of<K35>("256x256x64_s2_w8_m16_pp");
 constexpr KernelInfo kInfo36 = info_of<K36>("256x256x64_s2_w8_pp");
+constexpr KernelInfo kInfo37 = info_of<K37>("256x256x64_h5_w8_m16_pp");
 
 template <class C>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t stream) {
-  if constexpr (C::PP == 2)
+  if constexpr (C::PP == 3)
+    hipLaunchKernelGGL(gemm_pingpong_ring_kernel<C>, dim3(p.s.grid), dim3(C::THREADS), 0, stream,
+                       p);
+  else if constexpr (C::PP == 2)
     hipLaunchKernelGGL(gemm_pingpong64_kernel<C>, dim3(p.s.grid), dim3(C::THREADS), 0, stream, p);
   else if constexpr (C::PP)
     hipLaunchKernelGGL(gemm_pingpong_kernel<C>, dim3(p.s.grid), dim3(C::THREADS), 0, stream, p);
@@ -1234,7 +1409,10 @@ template <class C>
 int32_t occupancy_cfg() {
   int n = 0;
   hipError_t e;
-  if constexpr (C::PP == 2)
+  if constexpr (C::PP == 3)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_pingpong_ring_kernel<C>, C::THREADS,
+                                                     0);
+  else if constexpr (C::PP == 2)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_pingpong64_kernel<C>, C::THREADS, 0);
   else if constexpr (C::PP)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_pingpong_kernel<C>, C::THREADS, 0);

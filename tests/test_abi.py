@@ -286,19 +286,20 @@ def test_default_tail_rule(lib, M, N, K, mode):
 
 
 @pytest.mark.parametrize("M,N,K,kid,mode", [
-    (8192, 8192, 8192, 35, "data_parallel"),   # 4 tiles per CU: 64-wide stages
-    (16384, 16384, 16384, 35, "data_parallel"),
-    (8192, 8192, 4096, 35, "data_parallel"),
-    (4096, 4096, 4096, 35, "data_parallel"),   # one round exactly
-    (4608, 4608, 8192, 35, "dp_stream_k"),     # tiles left shared by stream-K
+    (8192, 8192, 8192, 37, "data_parallel"),   # 4 tiles per CU: 64-wide stages
+    (16384, 16384, 16384, 37, "data_parallel"),
+    (8192, 8192, 4096, 37, "data_parallel"),
+    (4096, 4096, 4096, 37, "data_parallel"),   # one round exactly
+    (4608, 4608, 8192, 37, "dp_stream_k"),     # tiles left shared by stream-K
     (4096, 4096, 1024, 27, "data_parallel"),   # K below 4096: 32-wide ring
     (10240, 10240, 2048, 27, "dp_stream_k"),
-    (2048, 2048, 16384, 27, "split"),          # fewer tiles than CUs: split-K
+    (2048, 2048, 16384, 37, "split"),          # fewer tiles than CUs: split-K
+    (1024, 1024, 65536, 37, "split"),
 ])
 def test_default_main_loop(lib, M, N, K, kid, mode):
-    """At least a round of 256x256 tiles with K >= 4096 takes the main loop
-    over 64-wide stages (whether or not the tiles left are shared); shorter K
-    and split plans keep the 32-wide ring."""
+    """At least a round of 256x256 tiles with K >= 4096, and split plans,
+    take the main loop over 64-wide stages in five half-stage slots (whether
+    or not the tiles left are shared); shorter K keeps the 32-wide ring."""
     text = gemm.gemm_f16_f32_abt_describe(M, N, K)
     assert f"kid={kid} " in text and f"mode={mode} " in text
     rows, k_iters, tiles = gemm.gemm_f16_schedule_dump(M, N, K)
@@ -340,7 +341,7 @@ def test_schedule_model_random_stream_k_plans(lib, monkeypatch):
     for _ in range(300):
         M, N = int(rng.integers(1, 3000)), int(rng.integers(1, 3000))
         K = int(rng.integers(1, 375)) * 8
-        kid = int(rng.choice([16, 18, 27, 28, 35, 36]))
+        kid = int(rng.choice([16, 18, 27, 28, 35, 36, 37]))
         plan = f"kid={kid},mode={int(rng.choice([2, 3]))},grid={int(rng.integers(1, 300))}"
         gemm.gemm_f16_set_plan_override(plan)
         rows, k_iters, tiles = gemm.gemm_f16_schedule_dump(M, N, K)

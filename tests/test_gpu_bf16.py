@@ -135,7 +135,7 @@ def test_default_rounds_then_stream_k(M, N, K):
     and K): integers bit-exact, uniform within tolerance, on sampled points."""
     text = gemm.gemm_f16_f32_abt_describe(M, N, K)
     log(f"  plan: {text}")
-    assert "mode=dp_stream_k" in text and "kid=35" in text
+    assert "mode=dp_stream_k" in text and "kid=37" in text
     A, B = inputs.integer_bf16(M, K, 191), inputs.integer_bf16(N, K, 192)
     check(A, B, run(A, B), "integer", f"{M}x{N}x{K} bf16 integer", sampled=True)
     A, B = inputs.uniform_bf16(M, K, 193), inputs.uniform_bf16(N, K, 194)
@@ -184,11 +184,11 @@ def test_k_zero_writes_zeros():
 
 PLANS = ["kid=16", "kid=18", "kid=27", "kid=27,grid=3", "kid=27,grid=2",
          "kid=27,mode=1,splits=3", "kid=27,mode=2,grid=37", "kid=16,mode=1,splits=2",
-         "kid=18,mode=2,grid=29", "kid=35", "kid=35,grid=3", "kid=35,mode=1,splits=3",
-         "kid=35,mode=3,grid=4",
-         # kernel ids not built for bfloat16 (a 32x32x16 form, and an id no
-         # kernel has): the plan keeps the shape rule's kernel
-         "kid=36", "kid=0"]
+         "kid=18,mode=2,grid=29", "kid=37", "kid=37,grid=3", "kid=37,mode=1,splits=3",
+         "kid=37,mode=3,grid=4", "kid=37,grid=1",
+         # kernel ids not built for bfloat16 (the comparison kernels, and an
+         # id no kernel has): the plan keeps the shape rule's kernel
+         "kid=35", "kid=36", "kid=0"]
 
 
 @pytest.mark.parametrize("plan", PLANS)

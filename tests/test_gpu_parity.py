@@ -198,13 +198,30 @@ def test_default_large_ragged(M, N, K):
     last row and column."""
     text = gemm.gemm_f16_f32_abt_describe(M, N, K)
     log(f"  plan: {text}")
-    assert "kid=35" in text
+    assert "kid=37" in text
     A, B = inputs.integer(M, K, 171), inputs.integer(N, K, 172)
     got = run(A, B)
     assert np.isfinite(got).all(), "C not fully written"
     rows, cols = sample_points(M, N, n_rand=2000)
     ref, _ = oracle.gemm_abt_elems(A, B, rows, cols)
     assert_exact(got[rows, cols], ref, f"{M}x{N}x{K} integer")
+
+
+@pytest.mark.parametrize("name", ["2048x2048x16384", "1024x1024x65536"])
+def test_long_k_five_slot_ring(name):
+    """The long-K workloads on the five-slot ring (kid 37) with the default
+    split: integers bit-exact at sampled points, k-block weights everywhere."""
+    M, N, K = WORKLOADS[name]
+    gemm.gemm_f16_set_plan_override("kid=37")
+    log(f"  plan: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
+    A, B = operands((M, N, K), "integer")
+    got = run(A, B)
+    rows, cols = sample_points(M, N, n_rand=2000)
+    ref, _ = oracle.gemm_abt_elems(A, B, rows, cols)
+    assert_exact(got[rows, cols], ref, f"{name} integer, kid 37")
+    w = 1 + (np.arange(K) // 64) % 7
+    got = run(inputs.ones(M, K), inputs.kblock_weights(N, K, 64))
+    assert np.all(got == float(w.sum())), f"k-block sum: got {np.unique(got)[:5]}"
 
 
 def test_hash_int_inputs():
@@ -357,8 +374,9 @@ def test_subnormal_inputs():
 # The kernels built: 16 (128x128x64) and 18 (64x64x64) run the symmetric
 # tiled loop; 27 (32-wide three-stage ring) and 28 (its 32x32x16 form, five
 # stages) the ping-pong loop; 35 and 36 (its 32x32x16 form) the ping-pong loop
-# over two 64-wide stages. Every one under every schedule mode.
-KIDS = [16, 18, 27, 28, 35, 36]
+# over two 64-wide stages; 37 the ping-pong loop over 64-wide stages kept as
+# separate A and B halves in five slots. Every one under every schedule mode.
+KIDS = [16, 18, 27, 28, 35, 36, 37]
 PLANS = [f"kid={k}" for k in KIDS] + [
     "kid=16,mode=1,splits=3", "kid=16,mode=2", "kid=16,mode=2,grid=37",
     "kid=16,mode=1,splits=3,grid=40", "kid=18,mode=1,splits=5", "kid=18,mode=2,grid=130",
@@ -371,11 +389,13 @@ PLANS = [f"kid={k}" for k in KIDS] + [
     "kid=27,grid=3", "kid=27,grid=1", "kid=27,mode=1,splits=2,grid=7", "kid=28,grid=4",
     "kid=35,grid=1", "kid=35,grid=3", "kid=35,mode=1,splits=2,grid=7", "kid=35,mode=1,splits=3",
     "kid=35,mode=2", "kid=35,mode=2,grid=37", "kid=36,grid=1", "kid=36,grid=3",
-    "kid=36,mode=1,splits=2,grid=7",
+    "kid=36,mode=1,splits=2,grid=7", "kid=37,grid=1", "kid=37,grid=3", "kid=37,mode=1,splits=3",
+    "kid=37,mode=1,splits=2,grid=7", "kid=37,mode=2", "kid=37,mode=2,grid=37",
     # Whole data-parallel rounds, then stream-K over the tiles left (the
     # forced grids make whole rounds at this size).
     "kid=27,mode=3,grid=4", "kid=16,mode=3,grid=7", "kid=18,mode=3,grid=50",
     "kid=28,mode=3,grid=5", "kid=35,mode=3,grid=4", "kid=36,mode=3,grid=4",
+    "kid=37,mode=3,grid=4",
 ]
 
 
@@ -412,7 +432,8 @@ def test_forced_plans_short_k(kid, K, monkeypatch):
 @pytest.mark.parametrize("plan", ["kid=28,grid=1", "kid=28,grid=2", "kid=27,grid=1",
                                   "kid=27,mode=1,splits=2,grid=3", "kid=35,grid=1",
                                   "kid=35,grid=2", "kid=35,mode=1,splits=2,grid=3",
-                                  "kid=36,grid=2"])
+                                  "kid=36,grid=2", "kid=37,grid=1",
+                                  "kid=37,mode=1,splits=2,grid=3"])
 @pytest.mark.parametrize("K", [24, 72, 200])
 def test_forced_plans_short_units(plan, K, monkeypatch):
     """Many short units per workgroup: units of one to a few k-tiles follow
