@@ -159,8 +159,10 @@ bool tiled_eligible(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
 //     loop with K split so tiles x splits fills the CUs (each share keeps
 //     >= 64 k-steps of 32);
 //   * smaller problems: 128x128 tiles, or 64x64 tiles when 128x128 ones
-//     would fill fewer than half the CUs, data-parallel (at these sizes the
-//     reduce pass of a split costs more than it gains);
+//     would fill fewer than half the CUs, or 32x32 tiles when even those
+//     number no more than the CUs (their per-workgroup chain of loads, MFMAs
+//     and stores is the shortest), data-parallel (at these sizes the reduce
+//     pass of a split costs more than it gains);
 //   * more 256x256 tiles than CUs, when the last round's idle CUs times the
 //     k-iterations is large enough: whole rounds data-parallel, the tiles
 //     left by stream-K (DP_SK).
@@ -243,6 +245,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
       mode = splits > 1 ? MODE_SPLIT : MODE_DATA_PARALLEL;
     } else {
       kid = 2 * cdiv(M, 128) * cdiv(N, 128) >= cus ? KID_128x128x64_S4_W4_M16
+            : cdiv(M, 32) * cdiv(N, 32) <= cus       ? KID_32x32x64_S5_W4_M16
                                                     : KID_64x64x64_S4_W4_M16;
     }
   }

@@ -21,7 +21,7 @@ namespace g16 {
 // two stages 64 wide in k (whole 128-byte rows per load), PP 3 its form with
 // the A and B halves of 64-wide stages in STAGES separate slots (five 32 KiB
 // slots: two and a half stages).
-// Built: the kernels the shape rule picks (16, 18, 27, 37) and three the
+// Built: the kernels the shape rule picks (16, 18, 27, 37, 38) and three the
 // plan override can select for comparisons on the same schedule: 35, the
 // two-stage form of 37's loop, and 28 and 36, the v_mfma_f32_32x32x16_f16
 // forms of the two ping-pong loops. Ids are stable: a removed variant's id is
@@ -33,10 +33,11 @@ namespace g16 {
   X(28, KID_256x256x32_S5_W8_PP, 256, 256, 32, 5, 2, 4, 32, 0, 1)      \
   X(35, KID_256x256x64_S2_W8_M16_PP, 256, 256, 64, 2, 2, 4, 16, 0, 2)  \
   X(36, KID_256x256x64_S2_W8_PP, 256, 256, 64, 2, 2, 4, 32, 0, 2)      \
-  X(37, KID_256x256x64_H5_W8_M16_PP, 256, 256, 64, 5, 2, 4, 16, 0, 3)
+  X(37, KID_256x256x64_H5_W8_M16_PP, 256, 256, 64, 5, 2, 4, 16, 0, 3)  \
+  X(38, KID_32x32x64_S5_W4_M16, 32, 32, 64, 5, 2, 2, 16, 0, 0)
 
 // Kernel ids also built for bfloat16 operands (the shape rule's picks).
-#define G16_BF16_KERNELS(X) X(16) X(18) X(27) X(37)
+#define G16_BF16_KERNELS(X) X(16) X(18) X(27) X(37) X(38)
 
 // Operand element types.
 enum DType : int32_t { DT_F16 = 0, DT_BF16 = 1 };
@@ -44,7 +45,7 @@ enum DType : int32_t { DT_F16 = 0, DT_BF16 = 1 };
 #define G16_KID_ENUM(id, name, ...) name = id,
 enum KernelId : int32_t {
   G16_TILED_KERNELS(G16_KID_ENUM)
-  KID_COUNT = 38,  // one past the largest id (ids in between may be unused)
+  KID_COUNT = 39,  // one past the largest id (ids in between may be unused)
   KID_GENERAL = 100  // any shape and alignment, 64 x 64 tiles, no LDS
 };
 #undef G16_KID_ENUM

@@ -1379,6 +1379,7 @@ constexpr KernelInfo kInfo28 = info_of<K28>("256x256x32_s5_w8_pp");
 constexpr KernelInfo kInfo35 = info_of<K35>("256x256x64_s2_w8_m16_pp");
 constexpr KernelInfo kInfo36 = info_of<K36>("256x256x64_s2_w8_pp");
 constexpr KernelInfo kInfo37 = info_of<K37>("256x256x64_h5_w8_m16_pp");
+constexpr KernelInfo kInfo38 = info_of<K38>("32x32x64_s5_w4_m16");
 
 template <class C>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t stream) {

@@ -341,8 +341,22 @@ def test_schedule_model_random_stream_k_plans(lib, monkeypatch):
     for _ in range(300):
         M, N = int(rng.integers(1, 3000)), int(rng.integers(1, 3000))
         K = int(rng.integers(1, 375)) * 8
-        kid = int(rng.choice([16, 18, 27, 28, 35, 36, 37]))
+        kid = int(rng.choice([16, 18, 27, 28, 35, 36, 37, 38]))
         plan = f"kid={kid},mode={int(rng.choice([2, 3]))},grid={int(rng.integers(1, 300))}"
         gemm.gemm_f16_set_plan_override(plan)
         rows, k_iters, tiles = gemm.gemm_f16_schedule_dump(M, N, K)
         assert check_schedule(rows.tolist(), k_iters, tiles) == [], (M, N, K, plan)
+
+
+@pytest.mark.parametrize("M,N,K,kid", [
+    (256, 256, 256, 38),      # 64 tiles of 32x32: one per CU or fewer
+    (512, 512, 512, 38),      # 256 tiles of 32x32
+    (512, 512, 2048, 38),
+    (640, 640, 1024, 18),     # 400 tiles of 32x32: 64x64 tiles instead
+    (1024, 1024, 1024, 18),
+    (2048, 2048, 2048, 16),   # enough 128x128 tiles for every CU twice
+])
+def test_default_small_tiles(lib, M, N, K, kid):
+    """Below a round of 256x256 tiles with short K the tile shrinks with the
+    problem: 128x128, then 64x64, then 32x32 while those fit the CUs."""
+    assert f"kid={kid} " in gemm.gemm_f16_f32_abt_describe(M, N, K)

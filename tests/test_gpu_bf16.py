@@ -185,7 +185,7 @@ def test_k_zero_writes_zeros():
 PLANS = ["kid=16", "kid=18", "kid=27", "kid=27,grid=3", "kid=27,grid=2",
          "kid=27,mode=1,splits=3", "kid=27,mode=2,grid=37", "kid=16,mode=1,splits=2",
          "kid=18,mode=2,grid=29", "kid=37", "kid=37,grid=3", "kid=37,mode=1,splits=3",
-         "kid=37,mode=3,grid=4", "kid=37,grid=1",
+         "kid=37,mode=3,grid=4", "kid=37,grid=1", "kid=38", "kid=38,mode=2,grid=29",
          # kernel ids not built for bfloat16 (the comparison kernels, and an
          # id no kernel has): the plan keeps the shape rule's kernel
          "kid=35", "kid=36", "kid=0"]

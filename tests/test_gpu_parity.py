@@ -371,15 +371,16 @@ def test_subnormal_inputs():
 
 # --- every kernel variant and schedule mode ---------------------------------
 
-# The kernels built: 16 (128x128x64) and 18 (64x64x64) run the symmetric
-# tiled loop; 27 (32-wide three-stage ring) and 28 (its 32x32x16 form, five
+# The kernels built: 16 (128x128x64), 18 (64x64x64) and 38 (32x32x64) run
+# the symmetric tiled loop; 27 (32-wide three-stage ring) and 28 (its 32x32x16 form, five
 # stages) the ping-pong loop; 35 and 36 (its 32x32x16 form) the ping-pong loop
 # over two 64-wide stages; 37 the ping-pong loop over 64-wide stages kept as
 # separate A and B halves in five slots. Every one under every schedule mode.
-KIDS = [16, 18, 27, 28, 35, 36, 37]
+KIDS = [16, 18, 27, 28, 35, 36, 37, 38]
 PLANS = [f"kid={k}" for k in KIDS] + [
     "kid=16,mode=1,splits=3", "kid=16,mode=2", "kid=16,mode=2,grid=37",
     "kid=16,mode=1,splits=3,grid=40", "kid=18,mode=1,splits=5", "kid=18,mode=2,grid=130",
+    "kid=38,mode=1,splits=3", "kid=38,mode=2,grid=37", "kid=38,mode=3,grid=9", "kid=38,grid=5",
     "kid=27,mode=1,splits=4", "kid=27,mode=2", "kid=27,mode=2,grid=29",
     "kid=28,mode=1,splits=2,grid=40", "kid=28,mode=2,grid=37",
     "kid=36,mode=1,splits=3", "kid=36,mode=2,grid=29",

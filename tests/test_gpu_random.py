@@ -30,8 +30,8 @@ from dense_fp16_gemm_03_amd import gemm  # noqa: E402
 DEV = torch.device("cuda:0")
 SEED = 20261202
 N_CASES = 200
-KIDS_F16 = (16, 18, 27, 28, 35, 36, 37)
-KIDS_BF16 = (16, 18, 27, 37)
+KIDS_F16 = (16, 18, 27, 28, 35, 36, 37, 38)
+KIDS_BF16 = (16, 18, 27, 37, 38)
 
 
 def draw(i):
