@@ -24,7 +24,9 @@ milliseconds, so `sustained` runs the headline call back to back for about two
 seconds after everything else and reports the probe clock, the per-call time
 and the board's power and power-limit residency over that loop.
 
-`configs` (unless --no-extras): the five workloads the way "SASS-Level Kernel
+`configs` (unless --no-extras; measured before the headline, so that the
+headline's warm-up starts on a running GPU rather than an idle one, unless
+--headline-first): the five workloads the way "SASS-Level Kernel
 Generation for Blackwell" measures (section "How we measured"): every call
 runs alone and the time of a call is its GPU time; the median over the last N
 calls is reported, over sweeps run in forward then reverse order. A short
@@ -606,6 +608,9 @@ def main():
                     help="run only a plain 1 GiB fp32 copy kernel (counter calibration)")
     ap.add_argument("--sweeps", type=int, default=2,
                     help="sweeps over the configs, alternately forward and reverse")
+    ap.add_argument("--headline-first", action="store_true",
+                    help="time the headline before the per-workload table (by default the "
+                         "table runs first)")
     ap.add_argument("--page-shapes", action="store_true",
                     help="also time the other shapes of the pages' table in `configs`")
     ap.add_argument("--vendor", action="store_true",
@@ -646,6 +651,33 @@ def main():
     C = torch.empty((M, N), dtype=torch.float32, device=dev)
 
     probe = Probe(torch, gemm, dev)
+
+    def run_configs():
+        spinner = Spinner(torch)
+        table = dict(inputs.WORKLOADS)
+        if args.page_shapes:
+            table.update(inputs.PAGE_SHAPES)
+        cache = {}
+        if name in table and args.inputs == "uniform":
+            cache[name] = (At, Bt, C)
+        t0 = time.perf_counter()
+        out = measure_configs(torch, gemm, table, dev, args.dtype, args.sweeps, spinner, cache,
+                              probe)
+        t1 = time.perf_counter()
+        del cache
+        torch.cuda.empty_cache()
+        log(f"[bench] configs measured in {t1 - t0:.1f} s (spin ahead of each call alone: "
+            f"{spinner.us} us)")
+        return out
+
+    # The per-workload table (the pages' method) runs before the headline
+    # unless --headline-first: the headline's warm-up calls then start on a
+    # GPU that has been running rather than idle (its clock right after idle
+    # dips for the first tens of milliseconds of full load; the probe clock
+    # of the timed calls is reported either way).
+    configs, pages_inputs = [], None
+    if not args.no_extras and not args.headline_first:
+        configs = run_configs()
     elapsed, kernel_us, sclk = time_headline(torch, gemm, At, Bt, C, args.steps, args.warmup,
                                              probe)
     ms_per_step = elapsed / args.steps * 1e3
@@ -672,23 +704,9 @@ def main():
         log(f"[bench] shader clock during the timed calls: {sclk} MHz "
             f"({roofline['frac_at_sclk'] * 100:.1f}% of the peak at that clock)")
 
-    configs, pages_inputs = [], None
     if not args.no_extras:
-        spinner = Spinner(torch)
-        table = dict(inputs.WORKLOADS)
-        if args.page_shapes:
-            table.update(inputs.PAGE_SHAPES)
-        cache = {}
-        if name in table and args.inputs == "uniform":
-            cache[name] = (At, Bt, C)
-        t0 = time.perf_counter()
-        configs = measure_configs(torch, gemm, table, dev, args.dtype, args.sweeps, spinner, cache,
-                                  probe)
-        t1 = time.perf_counter()
-        del cache
-        torch.cuda.empty_cache()
-        log(f"[bench] configs measured in {t1 - t0:.1f} s (spin ahead of each call alone: "
-            f"{spinner.us} us)")
+        if args.headline_first:
+            configs = run_configs()
         # The same workload on the input kind the pages time on (integers in
         # [-3, 3] from a hash of the index): context for the data-dependent
         # power draw, never the value.
