@@ -105,6 +105,7 @@ gemm_status_t validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t l
 struct Override {
   int32_t kid = -1, mode = -1, splits = -1, grid = -1, group = -1, xcd = -1;
   int32_t general = 0;  // 1: the general kernel, whatever the operands
+  int32_t direct = -1;  // 1: the direct kernel when the operands allow it; 0: never
   int32_t cus = -1;
 };
 
@@ -125,6 +126,7 @@ Override parse_override(const char* text) {
     else if (!std::strcmp(key, "group")) o.group = val;
     else if (!std::strcmp(key, "xcd")) o.xcd = val;
     else if (!std::strcmp(key, "general")) o.general = val;
+    else if (!std::strcmp(key, "direct")) o.direct = val;
     else if (!std::strcmp(key, "cus")) o.cus = val;
   }
   return o;
@@ -162,7 +164,8 @@ bool tiled_eligible(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
 //     would fill fewer than half the CUs, or 32x32 tiles when even those
 //     number no more than the CUs (their per-workgroup chain of loads, MFMAs
 //     and stores is the shortest), data-parallel (at these sizes the reduce
-//     pass of a split costs more than it gains);
+//     pass of a split costs more than it gains); and when 16x16 tiles number
+//     no more than the CUs and K <= 256, the direct kernel (no LDS);
 //   * more 256x256 tiles than CUs, when the last round's idle CUs times the
 //     k-iterations is large enough: whole rounds data-parallel, the tiles
 //     left by stream-K (DP_SK).
@@ -256,6 +259,15 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
   if (!tiled_eligible(M, N, K, A, lda, B, ldb, kid)) {
     if (allow_pack) return packed_plan(M, N, K, A, lda, B, ldb, C, ldc, cus, dt, kid, o);
     plan.kid = KID_GENERAL;
+    return plan;
+  }
+  // The smallest products (16x16 tiles no more than the CUs, K of one chunk
+  // of loads) take the direct kernel: no LDS, one wave a tile. Measured
+  // (kernel traces, same box): 256^3 3.64 -> 3.20 us against 32x32 tiles;
+  // ties at 256x512x256 and 128x128x1024, losses from 384^3 and at K = 1024.
+  const bool tiny = cdiv(M, 16) * cdiv(N, 16) <= cus && K <= 256;
+  if (o.direct == 1 || (tiny && o.kid < 0 && o.mode < 0 && o.direct != 0)) {
+    plan.kid = KID_DIRECT;
     return plan;
   }
   const KernelInfo* ki = kernel_info(kid);
@@ -510,7 +522,8 @@ gemm_status_t run(int32_t dt, int64_t M, int64_t N, int64_t K, const void* A, in
   }
   if (dev < 0) return GEMM_ERR_HIP;
   if (src == WS_STATIC && plan.workspace > 0 && ws == nullptr) return GEMM_ERR_HIP;
-  if (plan.kid != KID_GENERAL && !tiled_has(plan.kid, dt)) return GEMM_ERR_NOT_SUPPORTED;
+  if (plan.kid != KID_GENERAL && plan.kid != KID_DIRECT && !tiled_has(plan.kid, dt))
+    return GEMM_ERR_NOT_SUPPORTED;
   if (plan.workspace > 0 && !caller_ws) {
     // A library-owned workspace can be freed and replaced by a later call on
     // this stream; a captured graph would keep its old address. Calls being
@@ -569,6 +582,8 @@ gemm_status_t run(int32_t dt, int64_t M, int64_t N, int64_t K, const void* A, in
     }
     if (plan.pack_a || plan.pack_b) p.K = (int32_t)plan.kp;
   }
+  if (plan.kid == KID_DIRECT)
+    return launch_direct(dt, p, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
   return launch_tiled(plan.kid, dt, p, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
@@ -654,6 +669,14 @@ gemm_status_t gemm_f16_f32_abt_describe(int64_t M, int64_t N, int64_t K, char* b
   } else if (plan.kid == KID_GENERAL) {
     std::snprintf(buf, len, "M=%lld N=%lld K=%lld kernel=general_64x64", (long long)M,
                   (long long)N, (long long)K);
+  } else if (plan.kid == KID_DIRECT) {
+    char pack[64] = "";
+    if (plan.pack_a || plan.pack_b)
+      std::snprintf(pack, sizeof(pack), " pack=%s%s kp=%lld", plan.pack_a ? "A" : "",
+                    plan.pack_b ? "B" : "", (long long)plan.kp);
+    std::snprintf(buf, len, "M=%lld N=%lld K=%lld kernel=direct_16x16 kid=%d tiles=%lld%s",
+                  (long long)M, (long long)N, (long long)K, KID_DIRECT,
+                  (long long)(cdiv(M, 16) * cdiv(N, 16)), pack);
   } else {
     const KernelInfo* ki = kernel_info(plan.kid);
     const Sched& s = plan.s;
@@ -701,7 +724,7 @@ int64_t gemm_f16_schedule_dump(int64_t M, int64_t N, int64_t K, int64_t grid, in
   if (M <= 0 || N <= 0 || K <= 0 || cap < 0 || (cap > 0 && out == nullptr)) return -1;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return -1;
   Plan plan = reference_plan(M, N, K, -1);
-  if (plan.kid < 0 || plan.kid == KID_GENERAL) return -1;
+  if (plan.kid < 0 || plan.kid == KID_GENERAL || plan.kid == KID_DIRECT) return -1;
   Sched s = plan.s;
   if (grid > 0) {
     if ((s.mode == MODE_STREAM_K || s.mode == MODE_DP_SK) &&

@@ -46,7 +46,8 @@ enum DType : int32_t { DT_F16 = 0, DT_BF16 = 1 };
 enum KernelId : int32_t {
   G16_TILED_KERNELS(G16_KID_ENUM)
   KID_COUNT = 39,  // one past the largest id (ids in between may be unused)
-  KID_GENERAL = 100  // any shape and alignment, 64 x 64 tiles, no LDS
+  KID_GENERAL = 100,  // any shape and alignment, 64 x 64 tiles, no LDS
+  KID_DIRECT = 101    // 16 x 16 tiles, one wave each, no LDS (operands loadable directly)
 };
 #undef G16_KID_ENUM
 
@@ -84,6 +85,11 @@ hipError_t launch_tiled(int32_t kid, int32_t dt, const GemmParams& p, hipStream_
 
 // True when tiled kernel `kid` is built for operand type `dt`.
 bool tiled_has(int32_t kid, int32_t dt);
+
+// Launches the direct kernel (one 64-lane workgroup per 16x16 tile of C; A
+// and B must be loadable directly: 16-byte aligned rows of a multiple of 8
+// elements, K a multiple of 8).
+hipError_t launch_direct(int32_t dt, const GemmParams& p, hipStream_t stream);
 
 // Launches the general kernel over ceil(M/64) x ceil(N/64) workgroups.
 hipError_t launch_general(int32_t dt, const GemmParams& p, hipStream_t stream);

@@ -1314,6 +1314,70 @@ __global__ __launch_bounds__(256) void gemm_general_kernel(GemmParams p, int32_t
   }
 }
 
+// Direct kernel for the smallest problems: one wave per 16x16 tile of C and
+// no LDS. Each lane loads its own MFMA operand fragments (row l % 16 and
+// elements 8 (l / 16) .. +7 of every 32-wide k-step, for A and B) straight
+// from global memory with 16-byte buffer loads, all the k-steps of a chunk at
+// once, and accumulates them with v_mfma_f32_16x16x32 into two accumulators
+// (even and odd k-steps, added at the end), so that the dependent chain of
+// MFMAs is half as long. Rows past M or N and k-steps past K are masked by
+// out-of-range offsets (zeros, no memory access). Operands must follow the
+// tiled kernels' loading rules (16-byte aligned rows of a multiple of 8
+// elements). Each lane then holds 4 consecutive columns of one row of C and
+// stores them as one 16-byte write. Workgroups walk the tiles by stride.
+template <int DT>
+__global__ __launch_bounds__(64) void gemm_direct_kernel(GemmParams p, int32_t tiles_n,
+                                                         int64_t tiles) {
+  using M = Mma<16, DT>;
+  typedef typename M::frag_t frag_t;
+  constexpr int CH = 8;  // k-steps of 32 loaded at once
+  const int lane = threadIdx.x;
+  const int r = lane & 15;
+  const int kg = (lane >> 4) * 8;
+  const int nks = (p.K + 31) / 32;
+  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    const int m0 = (int)(t / tiles_n) * 16;
+    const int n0 = (int)(t % tiles_n) * 16;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.A + (int64_t)m0 * p.lda), (short)0, kNumRecords, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.B + (int64_t)n0 * p.ldb), (short)0, kNumRecords, kBufferWord3);
+    const uint32_t offa = m0 + r < p.M ? (uint32_t)(r * p.lda * 2 + kg * 2) : kMaskedOffset;
+    const uint32_t offb = n0 + r < p.N ? (uint32_t)(r * p.ldb * 2 + kg * 2) : kMaskedOffset;
+    f32x4 acc0 = {}, acc1 = {};
+    for (int c = 0; c < nks; c += CH) {
+      frag_t fa[CH], fb[CH];
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int k = (c + j) * 32;
+        const bool kin = k + kg < p.K;  // K is a multiple of 8: all or none of the lane's 8
+        fa[j] = __builtin_bit_cast(
+            frag_t, __builtin_amdgcn_raw_buffer_load_b128(ra, kin ? offa : kMaskedOffset, k * 2, 0));
+        fb[j] = __builtin_bit_cast(
+            frag_t, __builtin_amdgcn_raw_buffer_load_b128(rb, kin ? offb : kMaskedOffset, k * 2, 0));
+      }
+#pragma unroll
+      for (int j = 0; j < CH; j += 2) {
+        if (c + j < nks) acc0 = M::mma(fb[j], fa[j], acc0);
+        if (c + j + 1 < nks) acc1 = M::mma(fb[j + 1], fa[j + 1], acc1);
+      }
+    }
+    const f32x4 acc = acc0 + acc1;
+    const int m = m0 + M::acc_m(lane);
+    const int n = n0 + M::acc_n(0, lane);
+    if (m < p.M) {
+      float* crow = p.C + (int64_t)m * p.ldc;
+      if (n + 3 < p.N && p.c_vec4) {
+        __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(crow + n));
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (n + q < p.N) __builtin_nontemporal_store(acc[q], crow + n + q);
+      }
+    }
+  }
+}
+
 // Operand packing: one thread per 16-byte chunk (8 elements) of the packed
 // copy. The chunk's source bytes start at any 2-byte boundary, so the thread
 // loads the aligned 16-byte block holding its first element and, when a valid
@@ -1488,6 +1552,20 @@ hipError_t launch_general(int32_t dt, const GemmParams& p, hipStream_t stream) {
                        (int32_t)tiles_n, tiles);
   else
     hipLaunchKernelGGL(gemm_general_kernel<DT_F16>, dim3(grid), dim3(256), 0, stream, p,
+                       (int32_t)tiles_n, tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_direct(int32_t dt, const GemmParams& p, hipStream_t stream) {
+  const int64_t tiles_n = (p.N + 15) / 16;
+  const int64_t tiles = (p.M + 15) / 16 * tiles_n;
+  if (tiles <= 0) return hipSuccess;
+  const uint32_t grid = (uint32_t)min_of<int64_t>(tiles, (int64_t)1 << 20);
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL(gemm_direct_kernel<DT_BF16>, dim3(grid), dim3(64), 0, stream, p,
+                       (int32_t)tiles_n, tiles);
+  else
+    hipLaunchKernelGGL(gemm_direct_kernel<DT_F16>, dim3(grid), dim3(64), 0, stream, p,
                        (int32_t)tiles_n, tiles);
   return hipGetLastError();
 }

@@ -167,7 +167,8 @@ void gemm_f16_release_workspaces(void);
  * role 0 = the tile's only unit (stores C directly); role 1 = one of `shares`
  * units of a tile, `index` its position in k order (writes its partial tile
  * to workspace slot `index`; the reduce kernel sums the slots into C).
- * Returns the number of rows (writes at most `cap`), or -1 on bad arguments.
+ * Returns the number of rows (writes at most `cap`), or -1 on bad arguments or
+ * when the plan has no persistent schedule (the general and direct kernels).
  * *k_iters and *tiles (if non-NULL) receive the plan's k-iterations per tile
  * and its output-tile count. Used by tests to check that every (tile, k-iter)
  * is covered exactly once and that the shares of a tile are numbered 0..s-1
@@ -190,7 +191,8 @@ int32_t gemm_f16_lds_chunk(int32_t chunks_per_row, int32_t block_dim, int32_t ro
  *   kid=<tiled kernel id>  mode=<0 data-parallel, 1 split-K, 2 stream-K,
  *   3 whole data-parallel rounds then stream-K>  splits=<k-shares per tile>
  *   grid=<workgroups>  group=<tile rows per band>  xcd=<0|1 renumbering>
- *   cus=<compute units to plan for>  general=1 (the general kernel);
+ *   cus=<compute units to plan for>  general=1 (the general kernel)
+ *   direct=<1: the direct 16x16 kernel where the operands allow it, 0: never>;
  * keys the shape does not allow are ignored, so every plan stays correct.
  * NULL or "" restores the default rule. The override applies to every later
  * call in the process (all threads) and empties the plan cache. At first use

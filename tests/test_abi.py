@@ -194,7 +194,7 @@ SCHED_CASES = [
     (2048, 2048, 16384, None),
     (1024, 1024, 65536, None),
     (1024, 1024, 1024, None),
-    (256, 256, 256, None),
+    (256, 256, 512, None),
     (2048, 2048, 16384, "mode=2"),          # stream-K, even
     (1000, 1500, 4104, "mode=2"),           # stream-K, ranges cross tile ends
     (1000, 1500, 4104, "mode=2,grid=200"),
@@ -259,8 +259,15 @@ def test_planted_index_error_detected(lib, monkeypatch):
 
 
 def test_default_plans(lib):
-    """The five workloads take the tiled kernels with at most 256 workgroups."""
+    """The five workloads take the tiled kernels with at most 256 workgroups,
+    except 256^3, which takes the direct kernel (no persistent schedule: the
+    host model refuses it)."""
     for M, N, K in inputs.WORKLOADS.values():
+        if "direct" in gemm.gemm_f16_f32_abt_describe(M, N, K):
+            assert (M, N, K) == (256, 256, 256)
+            with pytest.raises(gemm.GemmError):
+                gemm.gemm_f16_schedule_dump(M, N, K)
+            continue
         rows, _, _ = gemm.gemm_f16_schedule_dump(M, N, K)
         assert rows[:, 0].max() < 256
 
@@ -349,7 +356,9 @@ def test_schedule_model_random_stream_k_plans(lib, monkeypatch):
 
 
 @pytest.mark.parametrize("M,N,K,kid", [
-    (256, 256, 256, 38),      # 64 tiles of 32x32: one per CU or fewer
+    (256, 256, 256, 101),     # 256 tiles of 16x16, K <= 256: the direct kernel
+    (256, 256, 512, 38),      # 64 tiles of 32x32: one per CU or fewer
+    (384, 384, 256, 38),      # 576 tiles of 16x16
     (512, 512, 512, 38),      # 256 tiles of 32x32
     (512, 512, 2048, 38),
     (640, 640, 1024, 18),     # 400 tiles of 32x32: 64x64 tiles instead
@@ -358,5 +367,6 @@ def test_schedule_model_random_stream_k_plans(lib, monkeypatch):
 ])
 def test_default_small_tiles(lib, M, N, K, kid):
     """Below a round of 256x256 tiles with short K the tile shrinks with the
-    problem: 128x128, then 64x64, then 32x32 while those fit the CUs."""
+    problem: 128x128, then 64x64, then 32x32 while those fit the CUs, then
+    the direct kernel's 16x16 for K <= 256."""
     assert f"kid={kid} " in gemm.gemm_f16_f32_abt_describe(M, N, K)

@@ -258,6 +258,22 @@ def test_ragged_shapes(M, N, K):
     assert_exact(run(Ai, Bi), ref, f"{M}x{N}x{K} integer")
 
 
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (300, 200, 136), (1, 1, 8), (17, 33, 1000),
+                                   (129, 250, 4104), (512, 512, 2048), (1000, 1300, 1001)])
+def test_direct_kernel(M, N, K):
+    """The direct kernel (16x16 tiles, no LDS) forced on ragged shapes, odd k
+    tails (K % 32 != 0) and, with K % 8 != 0, packed operands: integers
+    bit-exact, uniform within tolerance."""
+    gemm.gemm_f16_set_plan_override("direct=1")
+    log(f"  plan: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
+    Ai, Bi = inputs.integer(M, K, 161), inputs.integer(N, K, 162)
+    ref, _ = oracle.gemm_abt(Ai, Bi)
+    assert_exact(run(Ai, Bi), ref, f"direct {M}x{N}x{K} integer")
+    A, B = inputs.uniform(M, K, 163), inputs.uniform(N, K, 164)
+    ref, S = oracle.gemm_abt(A, B)
+    assert_tol(run(A, B), ref, S, f"direct {M}x{N}x{K} uniform")
+
+
 @pytest.mark.parametrize("M,N,K,force", [(100, 90, 13, False), (64, 64, 7, False),
                                          (5, 3, 1, False), (300, 200, 1001, True)])
 def test_general_kernel_odd_k(M, N, K, force, monkeypatch):
