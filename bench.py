@@ -7,8 +7,8 @@
 
 A step is one call of gemm_f16_f32_abt through the C ABI on synthetic
 operands already resident in HBM (uniform [-1, 1] fp16, seeds 1 and 2). The
-timed region is K back-to-back calls bracketed by device synchronisation;
-`value` is 2*M*N*K*K / elapsed in TFLOP/s. Each call is also bracketed by HIP
+timed region is --steps back-to-back calls bracketed by device
+synchronisation; `value` is 2*M*N*K * steps / elapsed in TFLOP/s. Each call is also bracketed by HIP
 events on the launch stream: their mean, median and minimum are the kernel's
 launch durations, from which `roofline.achieved` is computed against the fp16
 MFMA peak (2.5 PFLOP/s dense).
@@ -29,7 +29,8 @@ headline's warm-up starts on a running GPU rather than an idle one, unless
 --headline-first): the five workloads the way "SASS-Level Kernel
 Generation for Blackwell" measures (section "How we measured"): every call
 runs alone and the time of a call is its GPU time; the median over the last N
-calls is reported, over sweeps run in forward then reverse order. A short
+calls is reported, over four sweeps run in forward, reverse, forward and
+reverse order, as the pages interleave their runs. A short
 spin kernel is queued ahead of each timed call so that the call's events and
 kernels reach the GPU together: the events then bracket the call's kernels
 (and the gaps between them), not the host's launch latency. Beside it, the
@@ -606,8 +607,9 @@ def main():
                     help="skip the sustained loop with the board's telemetry")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB fp32 copy kernel (counter calibration)")
-    ap.add_argument("--sweeps", type=int, default=2,
-                    help="sweeps over the configs, alternately forward and reverse")
+    ap.add_argument("--sweeps", type=int, default=4,
+                    help="sweeps over the configs, alternately forward and reverse (the "
+                         "pages' fwd, rev, fwd, rev)")
     ap.add_argument("--headline-first", action="store_true",
                     help="time the headline before the per-workload table (by default the "
                          "table runs first)")
