@@ -209,8 +209,8 @@ void gemm_f16_set_plan_override(const char* text);
  * launches, 100 MHz * counters[0] / counters[1] is then the average shader
  * clock while they ran, which is what the MFMA peak scales with. The caller
  * zeroes the counters, keeps them alive while such launches are in flight,
- * and passes NULL to turn the probe off (the default). The general and
- * reduce kernels are not probed. */
+ * and passes NULL to turn the probe off (the default). The general, direct
+ * and reduce kernels are not probed. */
 void gemm_f16_set_clock_probe(unsigned long long* counters);
 
 
