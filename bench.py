@@ -3,7 +3,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8192^3] [--dtype f16|bf16]
                     [--inputs uniform|hash_int|integer] [--no-cpu-baseline] [--no-extras]
-                    [--sweeps S] [--page-shapes] [--vendor] [--calibrate-copy]
+                    [--sweeps S] [--page-shapes] [--shard-shapes] [--vendor]
+                    [--calibrate-copy]
 
 A step is one call of gemm_f16_f32_abt through the C ABI on synthetic
 operands already resident in HBM (uniform [-1, 1] fp16, seeds 1 and 2). The
@@ -74,7 +75,9 @@ PAGE_US = {"8192^3": (553.1 + 554.3) / 2, "1024^3": (4.64 + 4.67) / 2,
 # Timed calls per shape, as the pages time them ("How we measured").
 CALLS = {"256^3": 400, "1024^3": 400, "2048x2048x16384": 200, "1024x1024x65536": 200,
          "8192^3": 40, "1536^3": 400, "2048^3": 400, "3072x1280x2048": 400,
-         "4096x4096x1024": 300, "4096^3": 200, "8192x2048x4096": 200, "16384^3": 12}
+         "4096x4096x1024": 300, "4096^3": 200, "8192x2048x4096": 200, "16384^3": 12,
+         # one GPU's share of a workload split over 8 GPUs (not timed on the pages)
+         "8192^3 M/8": 200, "2048x2048x16384 K/8": 400, "1024x1024x65536 K/8": 400}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -615,6 +618,9 @@ def main():
                          "table runs first)")
     ap.add_argument("--page-shapes", action="store_true",
                     help="also time the other shapes of the pages' table in `configs`")
+    ap.add_argument("--shard-shapes", action="store_true",
+                    help="also time one GPU's share of each large workload split over 8 "
+                         "GPUs (M/8 for 8192^3, K/8 for the long-K shapes) in `configs`")
     ap.add_argument("--vendor", action="store_true",
                     help="also time hipBLASLt's fastest exact algorithm on every workload "
                          "(context only)")
@@ -640,7 +646,7 @@ def main():
     torch.cuda.set_device(dev)
 
     name = args.workload
-    all_shapes = {**inputs.WORKLOADS, **inputs.PAGE_SHAPES}
+    all_shapes = {**inputs.WORKLOADS, **inputs.PAGE_SHAPES, **inputs.SHARD_SHAPES}
     shape = all_shapes.get(name) or parse_shape(name)
     if shape is None:
         print(f"unknown workload {name!r}; known: {', '.join(all_shapes)}, or MxNxK",
@@ -659,6 +665,8 @@ def main():
         table = dict(inputs.WORKLOADS)
         if args.page_shapes:
             table.update(inputs.PAGE_SHAPES)
+        if args.shard_shapes:
+            table.update(inputs.SHARD_SHAPES)
         cache = {}
         if name in table and args.inputs == "uniform":
             cache[name] = (At, Bt, C)

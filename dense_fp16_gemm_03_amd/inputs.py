@@ -56,6 +56,15 @@ PAGE_SHAPES = {
     "16384^3": (16384, 16384, 16384),
 }
 
+# One GPU's share of each large workload split over 8 GPUs: 8192^3 by rows of
+# A (M / 8; no exchange once the inputs are placed), the long-K workloads by
+# K (K / 8; each GPU then holds a full fp32 partial C for one reduce-scatter).
+SHARD_SHAPES = {
+    "8192^3 M/8": (1024, 8192, 8192),
+    "2048x2048x16384 K/8": (2048, 2048, 2048),
+    "1024x1024x65536 K/8": (1024, 1024, 8192),
+}
+
 
 def uniform(rows: int, cols: int, seed: int) -> np.ndarray:
     """rows x cols binary16, i.i.d. uniform on [-1, 1]."""

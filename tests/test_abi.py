@@ -137,11 +137,11 @@ def test_packed_plans(lib, monkeypatch):
     text = gemm.gemm_f16_f32_abt_describe(M, N, K)
     assert "pack=AB kp=1008" in text and "kernel=64x64x64" in text
     assert gemm.gemm_f16_f32_abt_workspace_size(M, N, K) == 2 * (M * 1008 * 2)
-    M, N, K = 2048, 2048, 4095  # packed, and a split plan: partial tiles first
+    M, N, K = 1024, 1024, 8191  # packed, and a split plan: partial tiles first
     text = gemm.gemm_f16_f32_abt_describe(M, N, K)
-    assert "pack=AB kp=4096" in text and "mode=split" in text
-    parts = 64 * 2 * 256 * 256 * 4
-    assert gemm.gemm_f16_f32_abt_workspace_size(M, N, K) == parts + 2 * (M * 4096 * 2)
+    assert "pack=AB kp=8192" in text and "mode=split splits=4" in text and "kid=16" in text
+    parts = 64 * 4 * 128 * 128 * 4
+    assert gemm.gemm_f16_f32_abt_workspace_size(M, N, K) == parts + 2 * (M * 8192 * 2)
     assert "pack" not in gemm.gemm_f16_f32_abt_describe(2048, 2048, 4096)
     gemm.gemm_f16_set_plan_override("general=1")
     assert "general" in gemm.gemm_f16_f32_abt_describe(1024, 1024, 1001)
@@ -311,6 +311,28 @@ def test_default_main_loop(lib, M, N, K, kid, mode):
     assert f"kid={kid} " in text and f"mode={mode} " in text
     rows, k_iters, tiles = gemm.gemm_f16_schedule_dump(M, N, K)
     assert check_schedule(rows.tolist(), k_iters, tiles) == []
+
+
+@pytest.mark.parametrize("M,N,K,kid,mode,splits", [
+    (1024, 1024, 4096, 18, "data_parallel", 1),
+    (1024, 1024, 8192, 16, "split", 4),
+    (512, 512, 8192, 18, "split", 4),
+    (2048, 2048, 4096, 16, "data_parallel", 1),
+    (2048, 1024, 8192, 16, "split", 2),
+    (3072, 3072, 2048, 37, "data_parallel", 1),
+    (2048, 2048, 16384, 37, "split", 4),      # the rule's plan, kept
+    (1024, 1024, 65536, 37, "split", 16),
+    (256, 256, 1 << 20, 37, "split", 256),
+])
+def test_default_fewer_tiles_than_cus(lib, M, N, K, kid, mode, splits):
+    """Below a full round of 256x256 tiles the plan of least predicted time
+    is taken (64-wide kernels with 256x256, 128x128 or 64x64 tiles, any split
+    that keeps one round), unless the rule's own plan is predicted within
+    10% of it. A forced kernel or mode bypasses the prediction."""
+    text = gemm.gemm_f16_f32_abt_describe(M, N, K)
+    assert f"kid={kid} " in text and f"mode={mode} splits={splits} " in text, text
+    gemm.gemm_f16_set_plan_override("kid=37")
+    assert "kid=37 " in gemm.gemm_f16_f32_abt_describe(M, N, K)
 
 
 def test_plan_override_seen_on_many_threads(lib, monkeypatch):

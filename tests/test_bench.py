@@ -27,6 +27,20 @@ def test_shape_parsing():
         assert bench.parse_shape(bad) is None
 
 
+def test_shard_shapes_are_one_gpus_share():
+    """The shard shapes are 1/8 of a workload: M/8 of 8192^3 (same N and K),
+    K/8 of each long-K workload (same M and N); every timed shape has a call
+    count."""
+    W = inputs.WORKLOADS
+    for name, (m, n, k) in inputs.SHARD_SHAPES.items():
+        base, split = name.split(" ")
+        M, N, K = W[base]
+        assert (split, (m, n, k)) in (("M/8", (M // 8, N, K)), ("K/8", (M, N, K // 8)))
+        assert 2 * m * n * k * 8 == 2 * M * N * K
+    for table in (W, inputs.PAGE_SHAPES, inputs.SHARD_SHAPES):
+        assert all(name in bench.CALLS for name in table)
+
+
 def test_algorithmic_figures():
     flops, nbytes = bench.algorithmic(8192, 8192, 8192)
     assert flops == 2.0 * 8192**3

@@ -170,6 +170,46 @@ def test_page_shape_parity(name):
         assert_exact(got[rows, cols], ref, f"{name} integer")
 
 
+@pytest.mark.parametrize("name", list(inputs.SHARD_SHAPES))
+def test_shard_shape_parity(name):
+    """One GPU's share of each large workload split over 8 GPUs (M/8 of
+    8192^3, K/8 of the long-K shapes): integer inputs, bit-exact (sampled
+    rows, columns and points above 2048^3)."""
+    M, N, K = inputs.SHARD_SHAPES[name]
+    A, B = operands((M, N, K), "integer")
+    log(f"  plan: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
+    got = run(A, B)
+    if M * N * K <= 2048 ** 3:
+        ref, _ = oracle.gemm_abt(A, B)
+        assert_exact(got, ref, f"{name} integer")
+    else:
+        rows, cols = sample_points(M, N, n_rand=2000)
+        ref, _ = oracle.gemm_abt_elems(A, B, rows, cols)
+        assert_exact(got[rows, cols], ref, f"{name} integer")
+
+
+@pytest.mark.parametrize("M,N,K", [(1024, 1024, 4096), (512, 512, 8192), (2048, 1024, 8192),
+                                   (2048, 2048, 4096), (3072, 3072, 2048), (1000, 1100, 8200)])
+def test_default_fewer_tiles_than_cus(M, N, K):
+    """Default plans below a full round of 256x256 tiles (chosen by predicted
+    time: 64x64, 128x128 or 256x256 tiles, split or not): integers bit-exact
+    (sampled above 2048^3 products), uniform within tolerance."""
+    log(f"  plan: {gemm.gemm_f16_f32_abt_describe(M, N, K)}")
+    Ai, Bi = inputs.integer(M, K, 171), inputs.integer(N, K, 172)
+    got = run(Ai, Bi)
+    if M * N * K <= 2048 ** 3:
+        ref, _ = oracle.gemm_abt(Ai, Bi)
+        assert_exact(got, ref, f"{M}x{N}x{K} integer")
+    else:
+        rows, cols = sample_points(M, N, n_rand=2000)
+        ref, _ = oracle.gemm_abt_elems(Ai, Bi, rows, cols)
+        assert_exact(got[rows, cols], ref, f"{M}x{N}x{K} integer")
+    A, B = inputs.uniform(M, K, 173), inputs.uniform(N, K, 174)
+    rows, cols = sample_points(M, N, n_rand=2000)
+    ref, S = oracle.gemm_abt_elems(A, B, rows, cols)
+    assert_tol(run(A, B)[rows, cols], ref, S, f"{M}x{N}x{K} uniform")
+
+
 @pytest.mark.parametrize("M,N,K", [(4608, 4608, 8192), (4352, 4352, 4096)])
 def test_default_rounds_then_stream_k(M, N, K):
     """Shapes whose last round of 256x256 tiles is at most half full, with long
