@@ -26,12 +26,12 @@ constexpr int32_t kDefaultCUs = 256;  // MI355X: 8 XCDs x 32 CUs
 // integers, and a tile's first index plus its extent (at most 256, plus the
 // ring's masked tail stages in k) must not pass 2^31 - 1.
 constexpr int64_t kMaxDim = 0x7FFFFFFF - 1024;
-// Kernel for large tiles with K below 4096: 256x256 tiles, 16x16x32 MFMA,
+// Kernel for large tiles with K below 2048: 256x256 tiles, 16x16x32 MFMA,
 // two waves per SIMD in the ping-pong main loop over a 32-wide ring.
 constexpr int32_t KID_LARGE = KID_256x256x32_S3_W8_M16_PP;
 // The same tiles over 64-wide stages (whole 128-byte rows per load) held as
 // A and B halves in five LDS slots: for at least a round of tiles with
-// K >= 4096, and for long K split over the CUs.
+// K >= 2048, and for long K split over the CUs.
 constexpr int32_t KID_LARGE64 = KID_256x256x64_H5_W8_M16_PP;
 
 // Whether the tiles left after whole data-parallel rounds of 256x256 tiles
@@ -304,7 +304,11 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
     const int64_t t256 = cdiv(M, 256) * cdiv(N, 256);
     const int64_t k32 = cdiv(K, 32);
     if (t256 >= cus) {
-      kid = k32 >= 128 ? KID_LARGE64 : KID_LARGE;
+      // 64-wide stages from K = 2048 on: calls alone, one box, against the
+      // 32-wide ring: 4096^2 x 2048 64.2 -> 62.7 us, x 3072 89.4 -> 85.3,
+      // 8192^2 x 2048 234.7 -> 225.6. At K = 1024 they tie (4096^2: 39.8 /
+      // 40.0 us) or the ring wins (16384 x 4096: 139.0 / 141.3).
+      kid = k32 >= 64 ? KID_LARGE64 : KID_LARGE;
     } else if (k32 >= 128) {
       kid = KID_LARGE64;
       int64_t sp = cus / t256;

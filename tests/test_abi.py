@@ -298,13 +298,15 @@ def test_default_tail_rule(lib, M, N, K, mode):
     (8192, 8192, 4096, 37, "data_parallel"),
     (4096, 4096, 4096, 37, "data_parallel"),   # one round exactly
     (4608, 4608, 8192, 37, "dp_stream_k"),     # tiles left shared by stream-K
-    (4096, 4096, 1024, 27, "data_parallel"),   # K below 4096: 32-wide ring
-    (10240, 10240, 2048, 27, "dp_stream_k"),
+    (4096, 4096, 1024, 27, "data_parallel"),   # K below 2048: 32-wide ring
+    (4096, 4096, 2048, 37, "data_parallel"),
+    (10240, 10240, 2048, 37, "dp_stream_k"),
+    (10240, 10240, 1024, 27, "data_parallel"),
     (2048, 2048, 16384, 37, "split"),          # fewer tiles than CUs: split-K
     (1024, 1024, 65536, 37, "split"),
 ])
 def test_default_main_loop(lib, M, N, K, kid, mode):
-    """At least a round of 256x256 tiles with K >= 4096, and split plans,
+    """At least a round of 256x256 tiles with K >= 2048, and split plans,
     take the main loop over 64-wide stages in five half-stage slots (whether
     or not the tiles left are shared); shorter K keeps the 32-wide ring."""
     text = gemm.gemm_f16_f32_abt_describe(M, N, K)

@@ -230,12 +230,13 @@ def test_default_rounds_then_stream_k(M, N, K):
     assert np.all(got == float(w.sum())), f"k-block sum: got {np.unique(got)[:5]}"
 
 
-@pytest.mark.parametrize("M,N,K", [(4100, 4150, 4104), (8200, 8000, 8200)])
+@pytest.mark.parametrize("M,N,K", [(4100, 4150, 4104), (8200, 8000, 8200), (4100, 4150, 2056),
+                                   (6144, 6144, 2048)])
 def test_default_large_ragged(M, N, K):
-    """Large shapes with ragged M, N and K on the default plan (64-wide stages,
-    the tiles past whole rounds shared by stream-K, a partial last k-stage):
-    integers bit-exact on sampled rows, columns and points, including the
-    last row and column."""
+    """Large shapes with ragged M, N and K on the default plan (64-wide stages
+    from K = 2048, the tiles past whole rounds shared by stream-K, a partial
+    last k-stage): integers bit-exact on sampled rows, columns and points,
+    including the last row and column."""
     text = gemm.gemm_f16_f32_abt_describe(M, N, K)
     log(f"  plan: {text}")
     assert "kid=37" in text
