@@ -63,6 +63,27 @@ def draw(i):
                 pad_c=pad_c, off_c=off_c, dtype=dtype, plan=plan)
 
 
+N_DEFAULT_CASES = 60
+
+
+def draw_default(i):
+    """A random shape on the default plan: up to 1200 x 1200 with K up to 8200
+    (products of at most 4e9 multiply-adds), so the cases reach every branch
+    of the plan rule below a round of 256x256 tiles (direct kernel, 32x32
+    tiles, the predicted-time choice among 64x64, 128x128 and 256x256 tiles,
+    split or not, packed operands)."""
+    rng = np.random.default_rng([SEED, 7, i])
+    M, N = int(rng.integers(1, 1201)), int(rng.integers(1, 1201))
+    K = int(rng.integers(1, 8201))
+    K = max(1, min(K, int(4e9 // (M * N))))
+    c = draw(i)
+    c.update(M=M, N=N, plan="")
+    if c["off_a"] == 0 and c["off_b"] == 0:
+        K = max(8, K // 8 * 8)
+    c["K"] = K
+    return c
+
+
 def operand(bits_or_half, off, pad, dtype):
     """Device view of the operand inside a larger buffer (offset `off`
     elements into each row, `pad` spare elements after it)."""
@@ -80,8 +101,18 @@ def operand(bits_or_half, off, pad, dtype):
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_case(i, monkeypatch):
-    c = draw(i)
+    check_case(i, draw(i))
+
+
+@pytest.mark.parametrize("i", range(N_DEFAULT_CASES))
+def test_random_default_plan(i):
+    """Random shapes, strides, offsets and operand types on the default plan."""
+    check_case(1000 + i, draw_default(i))
+
+
+def check_case(i, c):
     print(f"[gpu test] random case {i}: {c}", flush=True)
+    print(f"  plan: {gemm.gemm_f16_f32_abt_describe(c['M'], c['N'], c['K'])}", flush=True)
     gemm.gemm_f16_set_plan_override(c["plan"])
     M, N, K = c["M"], c["N"], c["K"]
     if c["dtype"] == "bf16":
