@@ -12,6 +12,11 @@ About a quarter of the cases use unaligned pointers or strides (or K not a
 multiple of 8): the plan rule packs those operands into aligned copies when
 the product is large enough, else runs the general kernel; about one case in
 ten forces the general kernel.
+
+Two more families run on the default plan with the same strides, offsets and
+operand types: 60 shapes up to 1200 x 1200 (checked in full) and 16 large
+ones, M and N up to 6000 (checked on sampled rows, columns and points, after
+checking that every element of C was written).
 """
 import numpy as np
 import pytest
@@ -84,6 +89,26 @@ def draw_default(i):
     return c
 
 
+N_LARGE_CASES = 16
+
+
+def draw_large(i):
+    """A random large shape on the default plan: M, N in 1100..6000 and K up
+    to 8192 (products of at most 1.2e11 multiply-adds), which reaches whole
+    rounds of 256x256 tiles, the stream-K share of a last partial round, the
+    32- and 64-wide rings and, with unaligned operands, the packed path."""
+    rng = np.random.default_rng([SEED, 11, i])
+    M, N = int(rng.integers(1100, 6001)), int(rng.integers(1100, 6001))
+    K = int(rng.integers(8, 8193))
+    K = max(8, min(K, int(1.2e11 // (M * N))))
+    c = draw(2000 + i)
+    c.update(M=M, N=N, plan="")
+    if c["off_a"] == 0 and c["off_b"] == 0:
+        K = max(8, K // 8 * 8)
+    c["K"] = K
+    return c
+
+
 def operand(bits_or_half, off, pad, dtype):
     """Device view of the operand inside a larger buffer (offset `off`
     elements into each row, `pad` spare elements after it)."""
@@ -110,17 +135,39 @@ def test_random_default_plan(i):
     check_case(1000 + i, draw_default(i))
 
 
-def check_case(i, c):
+@pytest.mark.parametrize("i", range(N_LARGE_CASES))
+def test_random_large_default_plan(i):
+    """Random large shapes, strides, offsets and operand types on the default
+    plan, checked on sampled rows, columns and points (every element written,
+    none outside C)."""
+    check_case(3000 + i, draw_large(i), sampled=True)
+
+
+def sample(M, N, seed):
+    rng = np.random.default_rng(seed)
+    rows = [0, M - 1, M // 2, int(rng.integers(0, M))]
+    cols = [0, N - 1, N // 2, int(rng.integers(0, N))]
+    r = [np.full(N, x) for x in rows] + [np.arange(M) for _ in cols] + [rng.integers(0, M, 2000)]
+    c = [np.arange(N) for _ in rows] + [np.full(M, x) for x in cols] + [rng.integers(0, N, 2000)]
+    return np.concatenate(r), np.concatenate(c)
+
+
+def check_case(i, c, sampled=False):
     print(f"[gpu test] random case {i}: {c}", flush=True)
     print(f"  plan: {gemm.gemm_f16_f32_abt_describe(c['M'], c['N'], c['K'])}", flush=True)
     gemm.gemm_f16_set_plan_override(c["plan"])
     M, N, K = c["M"], c["N"], c["K"]
-    if c["dtype"] == "bf16":
+    bf16 = c["dtype"] == "bf16"
+    if bf16:
         A, B = inputs.integer_bf16(M, K, 1000 + i), inputs.integer_bf16(N, K, 2000 + i)
-        ref, _ = oracle.gemm_abt_bf16(A, B)
     else:
         A, B = inputs.integer(M, K, 1000 + i), inputs.integer(N, K, 2000 + i)
-        ref, _ = oracle.gemm_abt(A, B)
+    if sampled:
+        rows, cols = sample(M, N, i)
+        elems = oracle.gemm_abt_elems_bf16 if bf16 else oracle.gemm_abt_elems
+        ref, _ = elems(A, B, rows, cols)
+    else:
+        ref, _ = (oracle.gemm_abt_bf16 if bf16 else oracle.gemm_abt)(A, B)
     Av = operand(A, c["off_a"], c["pad_a"], c["dtype"])
     Bv = operand(B, c["off_b"], c["pad_b"], c["dtype"])
     off_c, pad_c = c["off_c"], c["pad_c"]
@@ -129,6 +176,9 @@ def check_case(i, c):
     torch.cuda.synchronize()
     out = Cbuf.cpu().numpy()
     got = out[:, off_c:off_c + N].astype(np.float64)
+    if sampled:
+        assert np.isfinite(got).all(), f"case {i}: C not fully written"
+        got = got[rows, cols]
     bad = got != ref
     assert not bad.any(), f"case {i}: {bad.sum()} mismatches, first at {np.argwhere(bad)[:3].tolist()}"
     assert np.isnan(out[:, :off_c]).all() and np.isnan(out[:, off_c + N:]).all(), \
