@@ -23,7 +23,12 @@ board's own telemetry (amdsmi gpu_metrics: gfx clocks, socket power, time at
 the package power limit) updates too slowly for a window of a few
 milliseconds, so `sustained` runs the headline call back to back for about two
 seconds after everything else and reports the probe clock, the per-call time
-and the board's power and power-limit residency over that loop.
+and the board's power and power-limit residency over that loop. The probe's
+workgroup 0 runs on one XCD; the board reports each XCD's clock, and they
+differ by several percent at the power limit. Every CU of the headline's plan
+has the same work, so the XCD with the slowest clock finishes last:
+`sustained.frac_at_slowest_xcd_clk` is the fraction of the peak at that
+XCD's mean clock over the window.
 
 `configs` (unless --no-extras; measured before the headline, so that the
 headline's warm-up starts on a running GPU rather than an idle one, unless
@@ -273,9 +278,17 @@ def sustained(torch, gemm, At, Bt, C, flops, probe, sampler, seconds=2.0):
            "tflops": round(flops / (us * 1e-6) / 1e12, 2), "sclk_mhz": mhz,
            "board": sampler.window(t0 + (t1 - t0) / 2, t1)}
     if mhz:
-        out["frac_at_sclk"] = round(flops / (us * 1e-6) / 1e12
-                                    / (PEAK_TFLOPS * mhz / PEAK_SCLK_MHZ), 4)
+        out["frac_at_sclk"] = frac_at_clock(flops, us, mhz)
+    per_xcd = (out["board"] or {}).get("gfx_clk_mhz_per_xcd")
+    if per_xcd:
+        out["frac_at_slowest_xcd_clk"] = frac_at_clock(flops, us, min(per_xcd))
     return out
+
+
+def frac_at_clock(flops, us, mhz):
+    """Fraction of the MFMA peak at shader clock `mhz` reached by `flops`
+    in `us` microseconds (the peak scales with the clock)."""
+    return round(flops / (us * 1e-6) / 1e12 / (PEAK_TFLOPS * mhz / PEAK_SCLK_MHZ), 4)
 
 
 class Spinner:

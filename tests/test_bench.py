@@ -101,3 +101,13 @@ def test_clock_window_summary():
     assert w["gfx_clk_mhz_per_xcd"] == [1650.0, 1550.0] * 4
     assert w["ppt_limited_frac"] == 0.4  # (500 - 100) / (2000 - 1000)
     assert s.window(5.0, 6.0) is None
+
+
+def test_fraction_at_a_clock():
+    """The peak scales with the shader clock: 2.5 PF at 2400 MHz, half of it
+    at 1200 MHz."""
+    flops = 2.0 * 8192 ** 3
+    us = flops / (bench.PEAK_TFLOPS * 1e12) * 1e6
+    assert bench.frac_at_clock(flops, us, bench.PEAK_SCLK_MHZ) == 1.0
+    assert bench.frac_at_clock(flops, 2 * us, bench.PEAK_SCLK_MHZ / 2) == 1.0
+    assert bench.frac_at_clock(flops, 2 * us, bench.PEAK_SCLK_MHZ) == 0.5
