@@ -207,7 +207,9 @@ void gemm_f16_set_plan_override(const char* text);
  * (s_memtime) to counters[0] and the 100 MHz real-time ticks (s_memrealtime)
  * to counters[1] between the workgroup's start and its end. Over a set of
  * launches, 100 MHz * counters[0] / counters[1] is then the average shader
- * clock while they ran, which is what the MFMA peak scales with. The caller
+ * clock while they ran, which is what the MFMA peak scales with (of the XCD
+ * workgroup 0 runs on: at the board's power limit the XCDs' clocks can differ
+ * by several percent). The caller
  * zeroes the counters, keeps them alive while such launches are in flight,
  * and passes NULL to turn the probe off (the default). The general, direct
  * and reduce kernels are not probed. */
