@@ -698,6 +698,50 @@ def test_threads_share_a_stream():
             assert np.array_equal(C.cpu().numpy(), refs[i]), f"shape {shapes[i]}"
 
 
+def test_threads_on_separate_streams():
+    """Two host threads, each on its own stream, run split plans at the same
+    time (the library then keeps one workspace per stream, and the two
+    streams' kernels may share the GPU). Every result equals the
+    single-stream one bit for bit."""
+    import threading
+
+    shapes = [(1024, 1024, 16384), (512, 768, 8192)]
+    ops, refs = [], []
+    for i, (M, N, K) in enumerate(shapes):
+        text = gemm.gemm_f16_f32_abt_describe(M, N, K)
+        log(f"  plan: {text}")
+        assert "mode=split" in text
+        A, B = inputs.uniform(M, K, 81 + i), inputs.uniform(N, K, 91 + i)
+        At, Bt = to_dev(A), to_dev(B)
+        ops.append((At, Bt))
+        refs.append(run(At, Bt))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in shapes]
+    outs = [[torch.full((M, N), np.nan, dtype=torch.float32, device=DEV) for _ in range(8)]
+            for (M, N, K) in shapes]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                for C in outs[i]:
+                    gemm.gemm_abt(*ops[i], C)
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(shapes))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i, Cs in enumerate(outs):
+        for C in Cs:
+            assert np.array_equal(C.cpu().numpy(), refs[i]), f"shape {shapes[i]}"
+
+
 @pytest.mark.parametrize("name", ["1024^3", "4096x4096x1024", "2048x2048x16384",
                                   "1024x1024x1001"])
 def test_graph_replay(name):
