@@ -248,6 +248,30 @@ def test_schedule_model_detects_dropped_unit(lib, monkeypatch, M, N, K, plan):
         assert check_schedule(rows + [rows[i]], k_iters, tiles) != []
 
 
+@pytest.mark.parametrize("grid", [1, 3, 7, 8, 9, 15, 100, 200, 243, 245, 250, 252, 256])
+def test_xcd_renumbering(lib, grid):
+    """Workgroup w runs on XCD w mod 8; the schedule renumbers workgroups so
+    that each XCD holds one contiguous block of units, for any grid: the
+    first tile of each workgroup (data-parallel, so unit v + n * grid) is a
+    permutation of 0 .. grid-1, contiguous and increasing within each XCD,
+    the XCDs' blocks in order, block sizes grid / 8 or one more."""
+    gemm.gemm_f16_set_plan_override("kid=18,mode=0")
+    rows, _, _ = gemm.gemm_f16_schedule_dump(4096, 4096, 256, grid)
+    first = {}
+    for w, tile in rows[:, :2].tolist():
+        first[w] = min(first.get(w, tile), tile)
+    assert sorted(first) == list(range(grid))
+    assert sorted(first.values()) == list(range(grid))
+    blocks = [[first[w] for w in range(x, grid, 8)] for x in range(min(grid, 8))]
+    for b in blocks:
+        assert b == list(range(b[0], b[0] + len(b)))
+        assert len(b) in (grid // 8, grid // 8 + 1)
+    for a, b in zip(blocks, blocks[1:]):
+        assert a[-1] + 1 == b[0]
+    if grid % 8 == 0:
+        assert all(first[w] == (w % 8) * (grid // 8) + w // 8 for w in range(grid))
+
+
 def test_planted_index_error_detected(lib, monkeypatch):
     """Swapping two shares' indices must fail the model (k order matters)."""
     rows, k_iters, tiles = gemm.gemm_f16_schedule_dump(1024, 1024, 65536)
